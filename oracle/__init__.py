@@ -1,0 +1,195 @@
+"""CPU oracle for the fused MLA decode query projection and assembly.
+
+TEST INFRASTRUCTURE ONLY. The product library and its Python binding never
+import, load or call anything here; only ``tests/``, the smoke check and the
+benchmark's CPU-baseline leg do. It shares no code with the HIP path.
+
+The arithmetic lives in ``mlaq_oracle.c`` (plain C99, built with ``gcc -O2
+-ffp-contract=off``); this module only builds it, loads it with ctypes and
+marshals numpy arrays. What it computes, and the page passages it follows, are
+stated at the top of ``mlaq_oracle.c``:
+
+* per-head product ``q_nope[m,h,:] . W[h,:,n]`` with an fp32 accumulator in
+  ascending k (sparkinfer PR #75 "[GG] Add BF16 MLA query projection and
+  assembly", sections "What" and "Contract");
+* bf16 round-to-nearest-even of the 512-wide projection, then, for E4M3
+  output, ``e4m3_satfinite(fp32(y) / q_scale)`` (same page, "Contract");
+* ``q_pe`` appended after the projection in the same 576-wide row (same page,
+  "What"; vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query assembly",
+  "What");
+* MXFP8 weights decoded exactly as ``e4m3(P) * 2^(S - 127)`` with one E8M0
+  scale per 32 contiguous n of each k row (sparkinfer PR #75, review thread on
+  ``api.py``: scale factors along n, N-major weight).
+
+Parity pins: every function here is checked against values the mathematics
+fixes (tests/test_oracle_codecs.py, tests/test_oracle_pins.py); none is
+"parity unpinned".
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+SRC = _HERE / "mlaq_oracle.c"
+LIB = _HERE / "libmlaq_oracle.so"
+
+WEIGHT_BF16, WEIGHT_MXFP8 = 0, 1
+OUT_BF16, OUT_E4M3 = 0, 1
+MX_BLOCK = 32
+
+GCC_FLAGS = ["-O2", "-std=gnu99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+
+
+def build(out: Path | None = None, src: Path | None = None) -> Path:
+    """Compile the oracle source (default ``mlaq_oracle.c``) with gcc into a
+    shared library and return its path."""
+    out = Path(out) if out is not None else LIB
+    src = Path(src) if src is not None else SRC
+    tmp = out.with_name(out.name + f".tmp{os.getpid()}")
+    cmd = ["gcc", *GCC_FLAGS, "-o", str(tmp), str(src), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib = None
+
+
+def _load(path: Path | None = None):
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(str(path)))
+    if _lib is None:
+        if not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
+            build()
+        _lib = _declare(ctypes.CDLL(str(LIB)))
+    return _lib
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    lib.mlaq_oracle_run.restype = ctypes.c_int
+    lib.mlaq_oracle_run.argtypes = [P, P, P, P, ctypes.c_float, P] + [ctypes.c_int] * 7 + [P, P, P, ctypes.c_int]
+    lib.mlaq_oracle_qscale.restype = ctypes.c_float
+    lib.mlaq_oracle_qscale.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t]
+    for name in ("mlaq_oracle_bf16_round", "mlaq_oracle_e4m3_encode", "mlaq_oracle_e4m3_decode",
+                 "mlaq_oracle_e8m0_decode"):
+        fn = getattr(lib, name)
+        fn.restype = None
+        fn.argtypes = [P, P, ctypes.c_size_t]
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def mla_query(q_nope, q_pe, w, w_scales=None, q_scale=None, *, weight_format=WEIGHT_BF16,
+              out_dtype=OUT_BF16, threads=1, diagnostics=True, lib_path=None):
+    """Run the oracle on host arrays.
+
+    Arguments are numpy arrays of raw bit patterns: ``q_nope`` uint16 (bf16)
+    ``[M,H,K]``, ``q_pe`` uint16 ``[M,H,R]``, ``w`` uint16 (bf16) or uint8
+    (E4M3) ``[H,K,N]``, ``w_scales`` uint8 (E8M0) ``[H,K,N/32]`` for MXFP8.
+    ``q_scale`` is a Python float (used only for E4M3 output).
+
+    Returns a dict: ``out`` (uint16 or uint8 ``[M,H,N+R]``) and, with
+    ``diagnostics``, ``acc`` (fp32 accumulators before rounding), ``s_abs``
+    (fp64 sum of |q*w|) and ``ref64`` (fp64 sum of q*w), each ``[M,H,N]``.
+    """
+    lib = _load(lib_path)
+    q_nope = _c(q_nope, np.uint16)
+    q_pe = _c(q_pe, np.uint16)
+    M, H, K = q_nope.shape
+    R = q_pe.shape[2]
+    if q_pe.shape[:2] != (M, H):
+        raise OracleError("q_pe shape does not match q_nope")
+    if weight_format == WEIGHT_BF16:
+        w = _c(w, np.uint16)
+        if w_scales is not None:
+            raise OracleError("BF16 weights take no scales")
+    else:
+        w = _c(w, np.uint8)
+        w_scales = _c(w_scales, np.uint8)
+    Hw, Kw, N = w.shape
+    if (Hw, Kw) != (H, K):
+        raise OracleError("weight shape does not match q_nope")
+    if weight_format == WEIGHT_MXFP8 and w_scales.shape != (H, K, N // MX_BLOCK):
+        raise OracleError("scale shape must be [H,K,N/32]")
+    if out_dtype == OUT_E4M3:
+        if q_scale is None:
+            raise OracleError("E4M3 output needs q_scale")
+        out = np.zeros((M, H, N + R), np.uint8)
+    else:
+        out = np.zeros((M, H, N + R), np.uint16)
+    acc = sabs = ref = None
+    if diagnostics:
+        acc = np.zeros((M, H, N), np.float32)
+        sabs = np.zeros((M, H, N), np.float64)
+        ref = np.zeros((M, H, N), np.float64)
+    rc = lib.mlaq_oracle_run(_ptr(q_nope), _ptr(q_pe), _ptr(w), _ptr(w_scales),
+                             float(q_scale if q_scale is not None else 1.0), _ptr(out),
+                             M, H, K, N, R, int(weight_format), int(out_dtype),
+                             _ptr(acc), _ptr(sabs), _ptr(ref), int(threads))
+    if rc != 0:
+        raise OracleError(f"mlaq_oracle_run failed with status {rc}")
+    res = {"out": out}
+    if diagnostics:
+        res.update(acc=acc, s_abs=sabs, ref64=ref)
+    return res
+
+
+def qscale_from_result(acc, q_pe, lib_path=None) -> float:
+    """amax/448 over the fp32 projection and q_pe (1.0 when amax is 0)."""
+    lib = _load(lib_path)
+    acc = _c(acc, np.float32)
+    q_pe = _c(q_pe, np.uint16)
+    return float(lib.mlaq_oracle_qscale(_ptr(acc), acc.size, _ptr(q_pe), q_pe.size))
+
+
+def _elementwise(name, arr, in_dtype, out_dtype, lib_path=None):
+    lib = _load(lib_path)
+    a = _c(arr, in_dtype)
+    out = np.empty(a.shape, out_dtype)
+    getattr(lib, name)(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def bf16_round(x, lib_path=None):
+    """fp32 array -> bf16 bit patterns (uint16), round to nearest even."""
+    return _elementwise("mlaq_oracle_bf16_round", x, np.float32, np.uint16, lib_path)
+
+
+def e4m3_encode(x, lib_path=None):
+    """fp32 array -> E4M3FN codes (uint8), nearest-even, saturating to +-448."""
+    return _elementwise("mlaq_oracle_e4m3_encode", x, np.float32, np.uint8, lib_path)
+
+
+def e4m3_decode(codes, lib_path=None):
+    """E4M3FN codes -> float64 values (NaN for 0x7F/0xFF)."""
+    return _elementwise("mlaq_oracle_e4m3_decode", codes, np.uint8, np.float64, lib_path)
+
+
+def e8m0_decode(codes, lib_path=None):
+    """E8M0 bytes -> float64 2^(b-127) (NaN for 0xFF)."""
+    return _elementwise("mlaq_oracle_e8m0_decode", codes, np.uint8, np.float64, lib_path)
+
+
+def bf16_to_f32(bits):
+    """Reinterpret bf16 bit patterns as float32 (a bit shift; not arithmetic)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)

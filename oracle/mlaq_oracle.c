@@ -1,0 +1,329 @@
+/*
+ * mlaq_oracle.c -- plain, slow, CPU oracle for the fused MLA decode query
+ * projection and assembly.
+ *
+ * TEST INFRASTRUCTURE ONLY. The product library never links, loads or calls
+ * this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do. It shares no code, header, table or helper with the HIP
+ * path: every codec below is written here from the OCP "8-bit Floating Point
+ * Specification (OFP8)" and "Microscaling Formats (MX) v1.0" definitions.
+ *
+ * What is computed, per decode token m < M and local head h < H:
+ *
+ *   acc[m,h,n]    = sum over k = 0..K-1 (ascending) of q_nope[m,h,k] * W[h,k,n]
+ *                   accumulated in fp32, each product formed exactly
+ *   y[m,h,n]      = bf16 round-to-nearest-even of acc
+ *   out[m,h,n]    = y                               BF16 output
+ *                 = e4m3_satfinite(fp32(y) / q_scale)  E4M3 output
+ *   out[m,h,N+r]  = q_pe[m,h,r]                     BF16 output (bit copy)
+ *                 = e4m3_satfinite(fp32(q_pe) / q_scale)  E4M3 output
+ *
+ * Sources (page title, then section):
+ *  - sparkinfer PR #75 "[GG] Add BF16 MLA query projection and assembly",
+ *    section "What": the per-head product q_nope x W_UK_T into a [M,H,576]
+ *    buffer with the 64-wide RoPE part appended in the same launch.
+ *  - same page, section "Contract": fp32 accumulation, rounding of the
+ *    512-wide projection to BF16 before any E4M3 conversion; E4M3 output takes
+ *    a q_scale, BF16 output takes none; K order may differ between
+ *    implementations, so the BF16 projection is not a bitwise contract.
+ *  - same page, review thread on api.py: the MXFP8 weight is N-major with its
+ *    scale factors along n (b_major "n", sf_axis "n"), batched over heads.
+ *  - vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query assembly", section
+ *    "What": native MXFP8 and materialized BF16 W_UK_T; the epilogue writes
+ *    [M,H,576] directly and appends q_pe; E4M3 output passes the query scale.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - the MXFP8 scale is one E8M0 byte per 32 contiguous n of each k row,
+ *    stored row-major as [H,K,N/32];
+ *  - "q / q_scale" is an IEEE fp32 division, correctly rounded;
+ *  - E4M3 is OCP E4M3FN (max 448, no infinities), conversion rounds to
+ *    nearest-even and saturates every finite or infinite overflow to +-448;
+ *    NaN maps to 0x7F with the sign kept;
+ *  - q_pe is quantized with the same per-tensor q_scale in E4M3 output.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * -pthread (no FMA contraction, so every fp32 add rounds once).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_WEIGHT_BF16 0
+#define ORACLE_WEIGHT_MXFP8 1
+#define ORACLE_OUT_BF16 0
+#define ORACLE_OUT_E4M3 1
+#define ORACLE_MX_BLOCK 32 /* MX block size along n (OCP MX v1.0) */
+
+/* ------------------------------------------------------------------------ */
+/* Codecs                                                                   */
+/* ------------------------------------------------------------------------ */
+
+static float f32_from_bits(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static uint32_t bits_from_f32(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+/* bf16 is the upper 16 bits of an IEEE binary32 pattern. */
+static float bf16_to_f32(uint16_t b) { return f32_from_bits((uint32_t)b << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even, written as the definition:
+ * take the two bf16 values that bracket x, return the nearer one, and on a
+ * tie the one whose last significand bit is 0. Past the largest finite bf16
+ * the upper neighbour is 2^128 (infinity), as in IEEE overflow rounding.
+ * NaN stays NaN (quiet, sign kept). */
+static uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = bits_from_f32(x);
+  if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);
+  uint16_t lo = (uint16_t)(u >> 16); /* neighbour toward zero */
+  if ((u & 0xFFFFu) == 0) return lo; /* x is exactly a bf16 */
+  uint16_t hi = (uint16_t)(lo + 1);  /* neighbour away from zero */
+  double ax = fabs((double)x);
+  double alo = fabs((double)bf16_to_f32(lo));
+  double ahi = ((hi & 0x7FFFu) == 0x7F80u) ? ldexp(1.0, 128) : fabs((double)bf16_to_f32(hi));
+  double dlo = ax - alo, dhi = ahi - ax;
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return (lo & 1u) ? hi : lo;
+}
+
+/* OCP E4M3FN decode: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there is
+ * no infinity. */
+static double e4m3_to_f64(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 0xF, m = c & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9); /* (m/8) * 2^(1-7) */
+  else
+    mag = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -mag : mag;
+}
+
+/* OCP MX E8M0 scale: 2^(b-127); 0xFF is NaN. */
+static double e8m0_to_f64(uint8_t b) { return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* Magnitudes of the 127 non-negative finite E4M3 codes 0x00..0x7E, filled
+ * from e4m3_to_f64 once. */
+static double g_e4m3_mag[0x7F];
+static pthread_once_t g_e4m3_once = PTHREAD_ONCE_INIT;
+static void e4m3_table_init(void) {
+  for (int c = 0; c < 0x7F; ++c) g_e4m3_mag[c] = e4m3_to_f64((uint8_t)c);
+}
+
+/* fp32 -> E4M3FN, round to nearest, ties to the even code, saturating:
+ * the result is the finite E4M3 value nearest to x (so everything past 448,
+ * infinity included, lands on 448). Written as a search over all finite
+ * codes. NaN -> 0x7F with the sign bit of x. */
+static uint8_t f32_to_e4m3_satfinite(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(0x7F | sign);
+  if (isinf(x)) return (uint8_t)(0x7E | sign);
+  pthread_once(&g_e4m3_once, e4m3_table_init);
+  double a = fabs((double)x);
+  int best = 0;
+  double bestd = a; /* distance to code 0 (+0.0) */
+  for (int c = 1; c < 0x7F; ++c) {
+    double d = fabs(a - g_e4m3_mag[c]);
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(best | sign);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The projection                                                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const uint16_t* q_nope; /* bf16 [M,H,K] */
+  const uint16_t* q_pe;   /* bf16 [M,H,R] */
+  const void* w;          /* bf16 [H,K,N] or e4m3 [H,K,N] */
+  const uint8_t* w_scales; /* e8m0 [H,K,N/32] (MXFP8 only) */
+  float q_scale;
+  void* out; /* bf16 or e4m3 [M,H,N+R] */
+  int M, H, K, N, R, weight_format, out_dtype;
+  float* acc_out;    /* optional fp32 [M,H,N] */
+  double* sabs_out;  /* optional fp64 [M,H,N]: sum |q*w| */
+  double* ref64_out; /* optional fp64 [M,H,N]: sum q*w in double */
+  int next_head;     /* work counter (heads), under the lock */
+  pthread_mutex_t lock;
+  int status;
+} oracle_job;
+
+/* Dequantized weight of head h, element (k,n), as an exact double. */
+static double weight_at(const oracle_job* j, int h, int k, int n) {
+  size_t idx = ((size_t)h * j->K + k) * j->N + n;
+  if (j->weight_format == ORACLE_WEIGHT_BF16)
+    return (double)bf16_to_f32(((const uint16_t*)j->w)[idx]);
+  {
+    uint8_t p = ((const uint8_t*)j->w)[idx];
+    uint8_t s = j->w_scales[((size_t)h * j->K + k) * (j->N / ORACLE_MX_BLOCK) + n / ORACLE_MX_BLOCK];
+    return e4m3_to_f64(p) * e8m0_to_f64(s);
+  }
+}
+
+/* Output conversion of one fp32 value (already bf16-valued for the
+ * projection) for E4M3 output. */
+static uint8_t to_e4m3_out(float v, float q_scale) { return f32_to_e4m3_satfinite(v / q_scale); }
+
+static void run_head(oracle_job* j, int h, double* wdq) {
+  const int K = j->K, N = j->N, R = j->R, H = j->H, OW = N + R;
+  /* Step 1: dequantize this head's weight slab W[h] (exact in double). */
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n) wdq[(size_t)k * N + n] = weight_at(j, h, k, n);
+
+  for (int m = 0; m < j->M; ++m) {
+    const uint16_t* q = j->q_nope + ((size_t)m * H + h) * K;
+    const uint16_t* pe = j->q_pe + ((size_t)m * H + h) * R;
+    size_t orow = ((size_t)m * H + h) * OW;
+    size_t arow = ((size_t)m * H + h) * N;
+    /* Step 2: contract over k in ascending order, fp32 accumulator. */
+    for (int n = 0; n < N; ++n) {
+      float acc = 0.0f;
+      double sabs = 0.0, ref = 0.0;
+      for (int k = 0; k < K; ++k) {
+        double p = (double)bf16_to_f32(q[k]) * wdq[(size_t)k * N + n]; /* exact */
+        acc = acc + (float)p;
+        sabs += fabs(p);
+        ref += p;
+      }
+      if (j->acc_out) j->acc_out[arow + n] = acc;
+      if (j->sabs_out) j->sabs_out[arow + n] = sabs;
+      if (j->ref64_out) j->ref64_out[arow + n] = ref;
+      /* Step 3: round the projection to bf16. */
+      uint16_t y = f32_to_bf16_rne(acc);
+      /* Step 4: write it, converting for E4M3 output. */
+      if (j->out_dtype == ORACLE_OUT_BF16)
+        ((uint16_t*)j->out)[orow + n] = y;
+      else
+        ((uint8_t*)j->out)[orow + n] = to_e4m3_out(bf16_to_f32(y), j->q_scale);
+    }
+    /* Step 5: append q_pe after the projection in the same row. */
+    for (int r = 0; r < R; ++r) {
+      if (j->out_dtype == ORACLE_OUT_BF16)
+        ((uint16_t*)j->out)[orow + N + r] = pe[r];
+      else
+        ((uint8_t*)j->out)[orow + N + r] = to_e4m3_out(bf16_to_f32(pe[r]), j->q_scale);
+    }
+  }
+}
+
+static void* worker(void* arg) {
+  oracle_job* j = (oracle_job*)arg;
+  double* wdq = (double*)malloc(sizeof(double) * (size_t)j->K * j->N);
+  if (!wdq) {
+    pthread_mutex_lock(&j->lock);
+    j->status = 3;
+    pthread_mutex_unlock(&j->lock);
+    return NULL;
+  }
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    int h = j->next_head++;
+    pthread_mutex_unlock(&j->lock);
+    if (h >= j->H) break;
+    run_head(j, h, wdq);
+  }
+  free(wdq);
+  return NULL;
+}
+
+/*
+ * Full fused call. Returns 0 on success, 1 on bad sizes or formats, 2 on
+ * missing buffers, 3 on host allocation failure. Heads are independent, so
+ * the work is split over `nthreads` threads by head; results do not depend
+ * on the thread count.
+ */
+int mlaq_oracle_run(const uint16_t* q_nope, const uint16_t* q_pe, const void* w,
+                    const uint8_t* w_scales, float q_scale, void* out, int M, int H, int K,
+                    int N, int R, int weight_format, int out_dtype, float* acc_out,
+                    double* sabs_out, double* ref64_out, int nthreads) {
+  oracle_job j;
+  if (M < 0 || H < 0 || K < 1 || N < ORACLE_MX_BLOCK || N % ORACLE_MX_BLOCK || R < 0) return 1;
+  if (weight_format != ORACLE_WEIGHT_BF16 && weight_format != ORACLE_WEIGHT_MXFP8) return 1;
+  if (out_dtype != ORACLE_OUT_BF16 && out_dtype != ORACLE_OUT_E4M3) return 1;
+  if (M == 0 || H == 0) return 0;
+  if (!q_nope || !w || !out || (R > 0 && !q_pe)) return 2;
+  if (weight_format == ORACLE_WEIGHT_MXFP8 && !w_scales) return 2;
+  memset(&j, 0, sizeof j);
+  j.q_nope = q_nope;
+  j.q_pe = q_pe;
+  j.w = w;
+  j.w_scales = w_scales;
+  j.q_scale = q_scale;
+  j.out = out;
+  j.M = M;
+  j.H = H;
+  j.K = K;
+  j.N = N;
+  j.R = R;
+  j.weight_format = weight_format;
+  j.out_dtype = out_dtype;
+  j.acc_out = acc_out;
+  j.sabs_out = sabs_out;
+  j.ref64_out = ref64_out;
+  pthread_mutex_init(&j.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > H) nthreads = H;
+  if (nthreads == 1) {
+    worker(&j);
+  } else {
+    pthread_t* tids = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int started = 0;
+    if (!tids) {
+      pthread_mutex_destroy(&j.lock);
+      return 3;
+    }
+    for (int t = 0; t < nthreads; ++t)
+      if (pthread_create(&tids[t], NULL, worker, &j) == 0) ++started;
+    if (started == 0) worker(&j);
+    for (int t = 0; t < started; ++t) pthread_join(tids[t], NULL);
+    free(tids);
+  }
+  pthread_mutex_destroy(&j.lock);
+  return j.status;
+}
+
+/*
+ * Per-tensor query scale for E4M3 output: amax / 448 over the layer's fp32
+ * result (the projection accumulators before bf16 rounding, and q_pe read as
+ * fp32); 1 when amax is 0. 448 is the largest finite E4M3FN value.
+ */
+float mlaq_oracle_qscale(const float* acc, size_t n_acc, const uint16_t* q_pe, size_t n_pe) {
+  float amax = 0.0f;
+  for (size_t i = 0; i < n_acc; ++i) {
+    float a = fabsf(acc[i]);
+    if (a > amax) amax = a;
+  }
+  for (size_t i = 0; i < n_pe; ++i) {
+    float a = fabsf(bf16_to_f32(q_pe[i]));
+    if (a > amax) amax = a;
+  }
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+/* Element-wise codec entry points, for pinning the codecs in tests. */
+void mlaq_oracle_bf16_round(const float* in, uint16_t* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
+}
+void mlaq_oracle_e4m3_encode(const float* in, uint8_t* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = f32_to_e4m3_satfinite(in[i]);
+}
+void mlaq_oracle_e4m3_decode(const uint8_t* in, double* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = e4m3_to_f64(in[i]);
+}
+void mlaq_oracle_e8m0_decode(const uint8_t* in, double* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = e8m0_to_f64(in[i]);
+}

@@ -1,0 +1,363 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``check_*`` function raises AssertionError when the oracle (optionally a
+specific build of it, ``lib``) disagrees with something the mathematics or an
+independent library fixes:
+
+* codecs against torch's own bf16 / float8_e4m3fn / float8_e8m0fnu casts and
+  against values the OCP OFP8 and MX v1.0 specifications fix;
+* the projection against layouts whose result is known exactly (identity,
+  one-hot, all-ones with power-of-two E8M0 scales, exactly representable
+  E4M3 outputs), against exact rational arithmetic on tiny shapes, and
+  against invariants (power-of-two scaling, head permutation, zero input,
+  head-count prefix, thread-count independence).
+
+The same functions run on deliberately broken builds of the oracle
+(tests/test_oracle_mutants.py) to show that each plausible mistake is caught.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import K_NOPE, MX_BLOCK, N_LATENT, R_ROPE, bf16_bits, e4m3_bits
+
+BF16_ONE = 0x3F80
+
+
+def _f32(bits_u16):
+    return oracle.bf16_to_f32(bits_u16)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    return bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+def _ulp_bf16(x):
+    """Spacing of bf16 values at |x| (normal range; 2^-133 below it)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -126)
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+# --------------------------------------------------------------------------
+# Codecs
+# --------------------------------------------------------------------------
+
+def check_e4m3_decode(lib=None):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes, lib_path=lib)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), "NaN codes differ from torch float8_e4m3fn"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin]), "E4M3 decode differs from torch float8_e4m3fn"
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+    # OCP OFP8 anchors: 1.0, max normal 448, min normal 2^-6, min subnormal 2^-9, NaN.
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9 and ours[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and np.sum(np.isnan(ours)) == 2
+
+
+def check_e8m0_decode(lib=None):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e8m0_decode(codes, lib_path=lib)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255]), "E8M0 decode differs from torch float8_e8m0fnu"
+    assert ours[127] == 1.0 and ours[120] == 2.0 ** -7 and ours[0] == 2.0 ** -127
+
+
+def check_bf16_round(lib=None):
+    rng = _rng(7)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    # Half of them on exact ties (low 16 bits = 0x8000), which exercise the even rule.
+    bits[::2] = (bits[::2] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    ours = oracle.bf16_round(x, lib_path=lib)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref), "bf16 RNE differs from torch's cast"
+    fixed = np.array([0x3F808000, 0x3F818000, 0x3F80FFFF, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000001,
+                      0x80000000], np.uint32).view(np.float32)
+    got = oracle.bf16_round(fixed, lib_path=lib)
+    assert list(got) == [0x3F80, 0x3F82, 0x3F81, 0x7F80, 0xFF80, 0x0000, 0x8000], [hex(v) for v in got]
+    nan = oracle.bf16_round(np.array([np.nan], np.float32), lib_path=lib)
+    assert (int(nan[0]) & 0x7F80) == 0x7F80 and (int(nan[0]) & 0x7F) != 0
+
+
+def check_e4m3_encode(lib=None):
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8), lib_path=lib)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    # Round trip of every finite code.
+    rt = oracle.e4m3_encode(dec[finite].astype(np.float32), lib_path=lib)
+    assert np.array_equal(rt, finite), "E4M3 encode(decode(c)) != c"
+    # Every midpoint between adjacent positive codes goes to the even code.
+    pos = np.arange(0, 0x7E, dtype=np.int64)
+    mids = ((dec[pos] + dec[pos + 1]) / 2).astype(np.float32)
+    got = oracle.e4m3_encode(mids, lib_path=lib).astype(np.int64)
+    want = np.where(pos % 2 == 0, pos, pos + 1)
+    assert np.array_equal(got, want), "E4M3 ties are not resolved to the even code"
+    got_neg = oracle.e4m3_encode(-mids, lib_path=lib).astype(np.int64)
+    assert np.array_equal(got_neg, want | 0x80)
+    # Against torch's cast on values inside the finite range (torch's cast is RNE there).
+    rng = _rng(11)
+    x = np.concatenate([
+        rng.standard_normal(50_000).astype(np.float32) * np.float32(40.0),
+        rng.standard_normal(50_000).astype(np.float32) * np.float32(0.01),
+        np.ldexp(rng.random(20_000), -rng.integers(0, 12, 20_000)).astype(np.float32),
+    ])
+    x = x[np.abs(x) < 448.0]
+    ours = oracle.e4m3_encode(x, lib_path=lib)
+    ref = torch.from_numpy(x.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref), "E4M3 encode differs from torch's cast in range"
+    # Saturation and specials (satfinite reading: everything past 448 -> 448).
+    special = np.array([449.0, 463.9, 464.0, 470.0, 480.0, 1e9, np.inf, -np.inf, -500.0, 0.0,
+                        -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 7.5 * 2.0 ** -9, 2.0 ** -11], np.float32)
+    got = list(oracle.e4m3_encode(special, lib_path=lib))
+    assert got == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x00, 0x02,
+                   0x08, 0x00], [hex(v) for v in got]
+    nan = oracle.e4m3_encode(np.array([np.nan, -np.nan], np.float32), lib_path=lib)
+    assert (int(nan[0]) & 0x7F) == 0x7F and (int(nan[1]) & 0x7F) == 0x7F
+
+
+# --------------------------------------------------------------------------
+# Projection: exact structured cases
+# --------------------------------------------------------------------------
+
+def _run(q, pe, w, s=None, q_scale=None, wf=0, od=0, lib=None, threads=1):
+    return oracle.mla_query(q, pe, w, s, q_scale, weight_format=wf, out_dtype=od, threads=threads,
+                            lib_path=lib)
+
+
+def check_identity_bf16(lib=None, H=16, M=3):
+    rng = _rng(21)
+    q = _rand_bf16(rng, (M, H, K_NOPE))
+    pe = _rand_bf16(rng, (M, H, R_ROPE))
+    w = np.zeros((H, K_NOPE, N_LATENT), np.uint16)
+    for h in range(H):
+        w[h, np.arange(K_NOPE), np.arange(K_NOPE) + 128 * (h % 4)] = BF16_ONE
+    out = _run(q, pe, w, lib=lib)["out"]
+    want = np.zeros((M, H, N_LATENT + R_ROPE), np.uint16)
+    for h in range(H):
+        want[:, h, 128 * (h % 4):128 * (h % 4) + K_NOPE] = q[:, h, :]
+    want[:, :, N_LATENT:] = pe
+    assert np.array_equal(out, want), "identity weights do not reproduce q_nope / q_pe bit-exactly"
+
+
+def check_identity_mxfp8(lib=None, H=16, M=2):
+    rng = _rng(22)
+    q = _rand_bf16(rng, (M, H, K_NOPE))
+    pe = _rand_bf16(rng, (M, H, R_ROPE))
+    w = np.zeros((H, K_NOPE, N_LATENT), np.uint8)
+    s = np.zeros((H, K_NOPE, N_LATENT // MX_BLOCK), np.uint8)
+    e = np.zeros((H, K_NOPE), np.int64)
+    for h in range(H):
+        for k in range(K_NOPE):
+            n = k + 128 * (h % 4)
+            w[h, k, n] = 0x38  # E4M3 1.0
+            e[h, k] = (h + 3 * k) % 7 - 5
+            s[h, k, :] = 127 + e[h, k]
+    out = _run(q, pe, w, s, wf=1, lib=lib)["out"]
+    want = np.zeros((M, H, N_LATENT + R_ROPE), np.uint16)
+    for h in range(H):
+        scaled = _f32(q[:, h, :]).astype(np.float64) * np.ldexp(1.0, e[h])[None, :]
+        want[:, h, 128 * (h % 4):128 * (h % 4) + K_NOPE] = bf16_bits(scaled.astype(np.float32))
+    want[:, :, N_LATENT:] = pe
+    assert np.array_equal(out, want), "MXFP8 identity (1.0 x 2^e) not exact"
+
+
+def check_one_hot(lib=None, H=11, M=4):
+    rng = _rng(23)
+    q = _rand_bf16(rng, (M, H, K_NOPE))
+    pe = _rand_bf16(rng, (M, H, R_ROPE))
+    w = np.zeros((H, K_NOPE, N_LATENT), np.uint16)
+    k0 = [(3 * h + 1) % K_NOPE for h in range(H)]
+    n0 = [(37 * h + 5) % N_LATENT for h in range(H)]
+    p = [h % 3 - 1 for h in range(H)]
+    for h in range(H):
+        w[h, k0[h], n0[h]] = bf16_bits(np.array([2.0 ** p[h]], np.float32))[0]
+    out = _run(q, pe, w, lib=lib)["out"]
+    want = np.zeros((M, H, N_LATENT + R_ROPE), np.uint16)
+    for h in range(H):
+        v = _f32(q[:, h, k0[h]]).astype(np.float64) * 2.0 ** p[h]
+        want[:, h, n0[h]] = bf16_bits(v.astype(np.float32))
+    want[:, :, N_LATENT:] = pe
+    assert np.array_equal(out, want), "one-hot weight lands in the wrong output lane"
+
+
+def check_scale_closed_form(lib=None, H=16, M=2):
+    """Payload 1.0 everywhere, E8M0 byte 127 - ((h+k+j) mod 9) for scale group j,
+    q = 2^-(k mod 4): the sum is an integer number of 2^-11 units, exact in any order."""
+    w = np.full((H, K_NOPE, N_LATENT), 0x38, np.uint8)
+    hh, kk, jj = np.meshgrid(np.arange(H), np.arange(K_NOPE), np.arange(N_LATENT // MX_BLOCK),
+                             indexing="ij")
+    d = (hh + kk + jj) % 9
+    s = (127 - d).astype(np.uint8)
+    qk = np.array([2.0 ** -(k % 4) for k in range(K_NOPE)], np.float32)
+    q = np.broadcast_to(bf16_bits(qk), (M, H, K_NOPE)).copy()
+    pe = np.broadcast_to(bf16_bits(np.arange(R_ROPE, dtype=np.float32) - 7), (M, H, R_ROPE)).copy()
+    out = _run(q, pe, w, s, wf=1, lib=lib)["out"]
+    units = np.zeros((H, N_LATENT), np.int64)  # multiples of 2^-11
+    for h in range(H):
+        for n in range(N_LATENT):
+            units[h, n] = sum(1 << (11 - (k % 4) - ((h + k + n // MX_BLOCK) % 9)) for k in range(K_NOPE))
+    exact = (units.astype(np.float64) / 2048.0).astype(np.float32)  # exact: < 2^24 units
+    want_proj = bf16_bits(exact)
+    for m in range(M):
+        assert np.array_equal(out[m, :, :N_LATENT], want_proj), "E8M0 scale applied to the wrong (k, n) group"
+        assert np.array_equal(out[m, :, N_LATENT:], pe[m])
+
+
+def check_e4m3_output(lib=None, H=8, M=3):
+    """Identity weights and q chosen as E4M3 values times 2^p with q_scale = 2^p:
+    every output code is known. One lane is pushed into (448, 480) to saturate."""
+    p = -3
+    rng = _rng(24)
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8), lib_path=lib)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes_q = rng.choice(finite, size=(M, H, K_NOPE))
+    codes_pe = rng.choice(finite, size=(M, H, R_ROPE))
+    q = bf16_bits((dec[codes_q] * 2.0 ** p).astype(np.float32))  # 4-bit values: exact in bf16
+    pe = bf16_bits((dec[codes_pe] * 2.0 ** p).astype(np.float32))
+    q[0, 0, 5] = bf16_bits(np.array([456.0 * 2.0 ** p], np.float32))[0]  # 456 is exact in bf16, above 448
+    w = np.zeros((H, K_NOPE, N_LATENT), np.uint16)
+    for h in range(H):
+        w[h, np.arange(K_NOPE), np.arange(K_NOPE) + 128 * (h % 4)] = BF16_ONE
+    out = _run(q, pe, w, q_scale=2.0 ** p, od=1, lib=lib)["out"]
+    want = np.zeros((M, H, N_LATENT + R_ROPE), np.uint8)
+    for h in range(H):
+        want[:, h, 128 * (h % 4):128 * (h % 4) + K_NOPE] = codes_q[:, h, :]
+    want[0, 0, 128 * 0 + 5] = 0x7E
+    want[:, :, N_LATENT:] = codes_pe
+    # +0 and -0 inputs: the projection of a -0 q lane through weight 1.0 is 0 + (-0) = +0.
+    proj_zero = (want[:, :, :N_LATENT] == 0x80)
+    want[:, :, :N_LATENT][proj_zero] = 0x00
+    assert np.array_equal(out, want), "E4M3 output codes differ from the exactly known ones"
+
+
+# --------------------------------------------------------------------------
+# Projection: exact rational brute force and invariants
+# --------------------------------------------------------------------------
+
+GAMMA_128 = (128 * 2.0 ** -24) / (1 - 128 * 2.0 ** -24)
+
+
+def check_brute_force(lib=None):
+    """H, M in 1..3 with exact Fraction sums: the fp32 accumulator is within the
+    standard recursive-summation bound gamma_K * sum|q w| of the exact value, and
+    the bf16 result is within one bf16 ulp of it (equal unless near a tie)."""
+    N, R = 64, 8
+    for wf in (0, 1):
+        for H in (1, 2, 3):
+            for M in (1, 2, 3):
+                rng = _rng(100 + 10 * H + M + 50 * wf)
+                q = _rand_bf16(rng, (M, H, K_NOPE))
+                pe = _rand_bf16(rng, (M, H, R))
+                if wf == 0:
+                    w = _rand_bf16(rng, (H, K_NOPE, N), std=K_NOPE ** -0.5)
+                    s = None
+                    wval = _f32(w).astype(np.float64)
+                else:
+                    w = e4m3_bits(rng.standard_normal((H, K_NOPE, N)).astype(np.float32) * 0.09)
+                    s = (127 + rng.integers(-8, 1, (H, K_NOPE, N // MX_BLOCK))).astype(np.uint8)
+                    dec = torch.from_numpy(w.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                    wval = dec * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(MX_BLOCK, axis=2)
+                res = _run(q, pe, w, s, wf=wf, lib=lib)
+                qv = _f32(q).astype(np.float64)
+                mismatches = 0
+                for m in range(M):
+                    for h in range(H):
+                        for n in range(N):
+                            terms = [Fraction(qv[m, h, k]) * Fraction(wval[h, k, n]) for k in range(K_NOPE)]
+                            exact = sum(terms, Fraction(0))
+                            sabs = sum(abs(t) for t in terms)
+                            acc = Fraction(float(res["acc"][m, h, n]))
+                            assert abs(acc - exact) <= Fraction(GAMMA_128) * sabs, (wf, H, M, m, h, n)
+                            assert abs(res["s_abs"][m, h, n] - float(sabs)) <= 1e-12 * float(sabs)
+                            y = float(_f32(res["out"][m, h, n:n + 1])[0])
+                            ex = float(exact)
+                            err = abs(Fraction(y) - exact)
+                            assert err <= Fraction(float(_ulp_bf16(ex))), (wf, H, M, m, h, n, y, ex)
+                            if err > Fraction(float(_ulp_bf16(ex))) / 2:
+                                mismatches += 1
+                assert mismatches <= max(1, (M * H * N) // 100), mismatches
+                assert np.array_equal(res["out"][:, :, N:], pe)
+
+
+def check_invariants(lib=None):
+    rng = _rng(31)
+    H, M = 16, 5
+    q = _rand_bf16(rng, (M, H, K_NOPE))
+    pe = _rand_bf16(rng, (M, H, R_ROPE))
+    w = _rand_bf16(rng, (H, K_NOPE, N_LATENT), std=K_NOPE ** -0.5)
+    base = _run(q, pe, w, lib=lib)
+    # Power-of-two scaling of q scales every accumulator exactly.
+    q4 = bf16_bits(_f32(q) * np.float32(4.0))
+    r4 = _run(q4, pe, w, lib=lib)
+    assert np.array_equal(r4["acc"], base["acc"] * np.float32(4.0)), "2^p scaling not exact"
+    # Permuting heads of (q, W, q_pe) permutes the output heads.
+    perm = rng.permutation(H)
+    rp = _run(q[:, perm], pe[:, perm], w[perm], lib=lib)
+    assert np.array_equal(rp["out"], base["out"][:, perm]), "head permutation does not commute"
+    # Zero q -> every projection lane is +0, whatever W holds.
+    rz = _run(np.zeros_like(q), pe, w, lib=lib)
+    assert not rz["out"][:, :, :N_LATENT].any(), "zero q does not give +0"
+    # q_pe lanes do not depend on W.
+    rw = _run(q, pe, np.zeros_like(w), lib=lib)
+    assert np.array_equal(rw["out"][:, :, N_LATENT:], base["out"][:, :, N_LATENT:])
+    # A prefix of heads (H = 11 of 16) gives the same heads' results.
+    r11 = _run(q[:, :11], pe[:, :11], w[:11], lib=lib)
+    assert np.array_equal(r11["out"], base["out"][:, :11]), "H=11 differs from the first 11 of H=16"
+    # A prefix of tokens gives the same tokens' results.
+    r3 = _run(q[:3], pe[:3], w, lib=lib)
+    assert np.array_equal(r3["out"], base["out"][:3])
+    # Thread count and repetition do not change a bit.
+    rt = _run(q, pe, w, lib=lib, threads=8)
+    assert np.array_equal(rt["out"], base["out"]) and np.array_equal(rt["acc"], base["acc"])
+    assert np.array_equal(_run(q, pe, w, lib=lib)["out"], base["out"])
+    # The fp32 accumulator stays within the summation bound of the fp64 sum.
+    assert np.all(np.abs(base["acc"] - base["ref64"]) <= 2 * GAMMA_128 * base["s_abs"])
+
+
+def check_qscale(lib=None):
+    rng = _rng(41)
+    acc = (rng.standard_normal((4, 16, N_LATENT)) * 3).astype(np.float32)
+    pe = _rand_bf16(rng, (4, 16, R_ROPE))
+    amax = max(float(np.max(np.abs(acc))), float(np.max(np.abs(_f32(pe)))))
+    assert oracle.qscale_from_result(acc, pe, lib_path=lib) == np.float32(amax) / np.float32(448.0)
+    assert oracle.qscale_from_result(np.zeros_like(acc), np.zeros_like(pe), lib_path=lib) == 1.0
+
+
+ALL_CHECKS = [check_e4m3_decode, check_e8m0_decode, check_bf16_round, check_e4m3_encode,
+              check_identity_bf16, check_identity_mxfp8, check_one_hot, check_scale_closed_form,
+              check_e4m3_output, check_brute_force, check_invariants, check_qscale]
+
+
+def check_e4m3_double_rounding(lib=None):
+    """E4M3 output rounds the projection to bf16 first. acc = 1 + 2^-4 + 2^-12 is
+    above the E4M3 midpoint between 1.0 and 1.125, but its bf16 rounding is the
+    midpoint itself, which then goes to the even code 0x38 (1.0)."""
+    H, M = 8, 1
+    q = np.zeros((M, H, K_NOPE), np.uint16)
+    q[:, :, 3] = bf16_bits(np.float32(1.0625))
+    q[:, :, 77] = bf16_bits(np.float32(2.0 ** -12))
+    pe = np.zeros((M, H, R_ROPE), np.uint16)
+    w = np.zeros((H, K_NOPE, N_LATENT), np.uint16)
+    w[:, 3, 200] = BF16_ONE
+    w[:, 77, 200] = BF16_ONE
+    res = _run(q, pe, w, q_scale=1.0, od=1, lib=lib)
+    assert float(res["acc"][0, 0, 200]) == 1.0625 + 2.0 ** -12
+    assert np.all(res["out"][:, :, 200] == 0x38), "E4M3 output skipped the bf16 rounding step"
+    assert not np.any(np.delete(res["out"][:, :, :N_LATENT], 200, axis=2))
+
+
+ALL_CHECKS.insert(9, check_e4m3_double_rounding)
