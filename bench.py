@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MLA decode query projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One *step* is a simulated decode step: 64 layers with distinct weight sets
+(32 with BF16 W_UK_T, 32 with MXFP8, alternating), H = 16 heads, M = 32
+tokens, E4M3 output with a per-layer q_scale = amax/448 of the fp32 result,
+the 64 fused calls captured as one hipGraph. Six copies of the 64 weight sets
+(582 MiB) are replayed round-robin, so every layer's weights come from HBM,
+not from the 256 MB Infinity Cache. It runs every step of the path: dispatch,
+weight streaming, q_nope staging, MXFP8 decode, contraction, rounding, the
+E4M3 epilogue, the q_pe append and the step composition. Per-layer seeds are
+100 * 1004 + layer (see workloads.make_inputs for the recipe).
+
+Printed JSON line (stdout, one line):
+  value       algorithmic HBM bytes of the step / step time, in GB/s
+  ms_per_step hipEvent time per replayed step
+  roofline    the dominant kernel (BF16-weight layer, M=32, E4M3 out): its
+              algorithmic bytes per launch / its average launch duration,
+              timed live with hipEvents over back-to-back cold launches,
+              against the 8 TB/s HBM peak
+  per_call    warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
+              MXFP8 weights (BF16 output), with the staged torch baseline
+  staged      the staged path (torch.bmm + copies + E4M3 quantization) of the
+              same step on the same GPU
+  cpu_baseline the CPU oracle timed on this host over a bounded sample of the
+              step's layers
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "µs per fused MLA query call + achieved HBM GB/s, H=16, M=1..32, BF16/MXFP8"
+HBM_PEAK_GBS = 8000.0
+H, M_STEP, LAYERS, COPIES = 16, 32, 64, 6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-per-call", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU-baseline sample")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# Device tensors
+# ----------------------------------------------------------------------------
+
+def dev_bf16(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_u8(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def dequant_bf16(torch, w, s):
+    """Materialized BF16 W_UK_T of an MXFP8 weight (exact), for the staged path."""
+    wf = w.view(torch.float8_e4m3fn).float()
+    sc = torch.exp2(s.float() - 127.0).repeat_interleave(32, dim=2)
+    return (wf * sc).to(torch.bfloat16)
+
+
+class Layer:
+    def __init__(self, torch, mq, wl, idx):
+        self.wf = mq.MLAQ_WEIGHT_BF16 if idx % 2 == 0 else mq.MLAQ_WEIGHT_MXFP8
+        inp = wl.make_inputs(wl.SEED["c4"] * 100 + idx, H=H, weight_format=self.wf, M_draw=M_STEP)
+        self.q = dev_bf16(torch, inp.q_nope)
+        self.pe = dev_bf16(torch, inp.q_pe)
+        if self.wf == mq.MLAQ_WEIGHT_BF16:
+            self.w_host, self.s_host = inp.w, None
+        else:
+            self.w_host, self.s_host = inp.w, inp.w_scales
+        self.out = torch.empty((M_STEP, H, mq.ROW), dtype=torch.uint8, device="cuda")
+        self.qs = torch.empty((1,), dtype=torch.float32, device="cuda")
+        self.bytes = wl.algorithmic_bytes(M_STEP, H, self.wf, mq.MLAQ_OUT_E4M3)
+
+    def weights_on_device(self, torch, mq):
+        if self.wf == mq.MLAQ_WEIGHT_BF16:
+            return dev_bf16(torch, self.w_host), None
+        return dev_u8(torch, self.w_host), dev_u8(torch, self.s_host)
+
+
+def step_graph(torch, mq, layers, wcopy, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+            for L, (w, s) in zip(layers, wcopy):
+                mq.mlaq_run(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3)
+    return g
+
+
+def time_graphs(torch, graphs, steps, warmup, per_step_units=1):
+    """hipEvent time of `steps` round-robin replays, ms per replay / unit."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record(st)
+    t1.synchronize()
+    return t0.elapsed_time(t1) / steps / per_step_units
+
+
+# ----------------------------------------------------------------------------
+# Legs
+# ----------------------------------------------------------------------------
+
+def decode_step_leg(torch, mq, wl, args):
+    log(f"[bench] building {LAYERS} layers x {COPIES} weight copies (H={H}, M={M_STEP})")
+    layers = [Layer(torch, mq, wl, i) for i in range(LAYERS)]
+    copies = [[L.weights_on_device(torch, mq) for L in layers] for _ in range(COPIES)]
+    for i in (mq.MLAQ_WEIGHT_BF16, mq.MLAQ_WEIGHT_MXFP8):
+        mq.mlaq_prewarm(H, [M_STEP], i, mq.MLAQ_OUT_E4M3)
+    # Per-layer q_scale = amax / 448 of the fp32 result (projection and q_pe),
+    # computed with torch on the GPU from copy 0.
+    wbf = []
+    for L, (w, s) in zip(layers, copies[0]):
+        wb = w if s is None else dequant_bf16(torch, w, s)
+        wbf.append(wb)
+        acc = torch.bmm(L.q.transpose(0, 1).float().contiguous(), wb.float().contiguous())
+        amax = torch.maximum(acc.abs().max(), L.pe.float().abs().max())
+        L.qs.copy_((amax / 448.0).reshape(1))
+    torch.cuda.synchronize()
+    weight_bytes = sum(w.numel() * w.element_size() + (0 if s is None else s.numel()) for w, s in copies[0])
+    log(f"[bench] weights per copy {weight_bytes / 2**20:.1f} MiB, total {COPIES * weight_bytes / 2**20:.0f} MiB")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graphs = [step_graph(torch, mq, layers, copies[c], stream) for c in range(COPIES)]
+    torch.cuda.synchronize()
+    log("[bench] step graphs captured")
+    ms = time_graphs(torch, graphs, args.steps, args.warmup)
+    step_bytes = sum(L.bytes for L in layers)
+    log(f"[bench] fused step: {ms * 1e3:.2f} us/step, {ms * 1e3 / LAYERS:.3f} us/layer, "
+        f"{step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+
+    # Dominant kernel alone: the 32 BF16-weight layers back to back (cold).
+    dom_graphs = []
+    for c in range(COPIES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                for L, (w, s) in zip(layers, copies[c]):
+                    if L.wf == mq.MLAQ_WEIGHT_BF16:
+                        mq.mlaq_run(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3)
+        dom_graphs.append(g)
+    torch.cuda.synchronize()
+    n_bf = sum(1 for L in layers if L.wf == mq.MLAQ_WEIGHT_BF16)
+    dom_ms = time_graphs(torch, dom_graphs, args.steps, args.warmup, per_step_units=n_bf)
+    dom_bytes = wl.algorithmic_bytes(M_STEP, H, mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_E4M3)
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    log(f"[bench] dominant kernel (bf16 W, M=32, E4M3): {dom_ms * 1e3:.3f} us/launch, {dom_gbs:.1f} GB/s")
+    del dom_graphs
+
+    # Staged path of the same step: bmm + copy + copy + E4M3 quantization.
+    staged_graphs = []
+    tmp_out = [torch.empty((M_STEP, H, mq.ROW), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    staged_w = [wbf] + [[w if s is None else dequant_bf16(torch, w, s) for w, s in copies[c]]
+                        for c in range(1, COPIES)]
+    torch.cuda.synchronize()
+    for c in range(COPIES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for L, wb, ob in zip(layers, staged_w[c], tmp_out):
+                    t = torch.bmm(L.q.transpose(0, 1).contiguous(), wb)
+                    ob[..., :512].copy_(t.transpose(0, 1))
+                    ob[..., 512:].copy_(L.pe)
+                    L.out.view(torch.float8_e4m3fn).copy_((ob.float() / L.qs).clamp(-448.0, 448.0))
+        staged_graphs.append(g)
+    torch.cuda.synchronize()
+    staged_ms = time_graphs(torch, staged_graphs, args.steps, args.warmup)
+    log(f"[bench] staged step: {staged_ms * 1e3:.2f} us/step ({staged_ms / ms:.2f}x fused)")
+    del staged_graphs, staged_w, tmp_out, wbf
+    torch.cuda.synchronize()
+    return {
+        "layers": layers, "ms": ms, "step_bytes": step_bytes, "dom_ms": dom_ms, "dom_bytes": dom_bytes,
+        "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes,
+    }
+
+
+def per_call_leg(torch, mq, wl, reps=100, replays=20):
+    res = {}
+    for name, wf, seed in (("bf16", mq.MLAQ_WEIGHT_BF16, wl.SEED["c1"]), ("mxfp8", mq.MLAQ_WEIGHT_MXFP8, wl.SEED["c3"])):
+        inp = wl.make_inputs(seed, H=H, weight_format=wf, M_draw=32)
+        w = dev_bf16(torch, inp.w) if wf == mq.MLAQ_WEIGHT_BF16 else dev_u8(torch, inp.w)
+        s = None if wf == mq.MLAQ_WEIGHT_BF16 else dev_u8(torch, inp.w_scales)
+        wb = w if s is None else dequant_bf16(torch, w, s)
+        rows = {}
+        for M in (1, 2, 4, 8, 16, 32):
+            q = dev_bf16(torch, inp.q_nope[:M])
+            pe = dev_bf16(torch, inp.q_pe[:M])
+            out = torch.empty((M, H, mq.ROW), dtype=torch.bfloat16, device="cuda")
+            mq.mlaq_prewarm(H, [M], wf, mq.MLAQ_OUT_BF16)
+            stream = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                    for _ in range(reps):
+                        mq.mlaq_run(q, pe, w, s, None, out, wf, mq.MLAQ_OUT_BF16)
+            us = time_graphs(torch, [g], replays, 3, per_step_units=reps) * 1e3
+            gs = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(gs, stream=stream):
+                    for _ in range(reps):
+                        t = torch.bmm(q.transpose(0, 1).contiguous(), wb)
+                        out[..., :512].copy_(t.transpose(0, 1))
+                        out[..., 512:].copy_(pe)
+            us_staged = time_graphs(torch, [gs], replays, 3, per_step_units=reps) * 1e3
+            nbytes = wl.algorithmic_bytes(M, H, wf, mq.MLAQ_OUT_BF16)
+            rows[str(M)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                            "staged_us": round(us_staged, 3)}
+            log(f"[bench] per-call {name} M={M}: {us:.3f} us ({rows[str(M)]['gbs']} GB/s), staged {us_staged:.3f} us")
+            del g, gs
+        res[name] = rows
+    return res
+
+
+def cpu_baseline_leg(wl, layers, budget_s):
+    """The CPU oracle on the step's layers, until the time budget is spent."""
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    done_bytes, t_used, n = 0, 0.0, 0
+    for idx in range(LAYERS):
+        wf = 0 if idx % 2 == 0 else 1
+        inp = wl.make_inputs(wl.SEED["c4"] * 100 + idx, H=H, weight_format=wf, M_draw=M_STEP)
+        qs = float(layers[idx].qs.item()) if layers is not None else 1.0
+        t0 = time.perf_counter()
+        oracle.mla_query(inp.q_nope, inp.q_pe, inp.w, inp.w_scales, qs, weight_format=wf, out_dtype=1,
+                         threads=threads, diagnostics=False)
+        t_used += time.perf_counter() - t0
+        done_bytes += wl.algorithmic_bytes(M_STEP, H, wf, 1)
+        n += 1
+        if t_used >= budget_s:
+            break
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {LAYERS} decode-step layers (H=16, M=32, E4M3 out, BF16/MXFP8 alternating), "
+                      f"{t_used:.1f} s with {threads} threads on {cpu} (nproc {os.cpu_count()}); "
+                      f"{t_used / n * 1e3:.1f} ms per layer vs GPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the op shards by heads "
+              f"with no exchange, so per-GPU work is the single-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mla_decode_query_amd as mq
+    import workloads as wl
+
+    if not mq.LIB_PATH.exists():
+        from mla_decode_query_amd import _build
+
+        _build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"[bench] device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+    step = decode_step_leg(torch, mq, wl, args)
+    per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+    ms = step["ms"]
+    value = step["step_bytes"] / (ms * 1e-3) / 1e9
+    dom_gbs = step["dom_bytes"] / (step["dom_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step: 64 layers (32 BF16 + 32 MXFP8 W_UK_T, alternating), H=16, M=32, "
+                               "E4M3 out, one hipGraph per step, 6 rotated weight copies (cold HBM)",
+                   "heads": H, "tokens": M_STEP, "layers": LAYERS, "nope": 128, "latent": 512, "rope": 64,
+                   "bytes_per_step": step["step_bytes"]},
+        "us_per_layer": round(ms * 1e3 / LAYERS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles>",
+                     "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"]},
+        "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3)},
+        "per_call": per_call,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * mlaq.h -- C ABI of libmlaq, the MI355X (gfx950) fused MLA decode query
+ * projection and assembly.
+ *
+ * The operation (sparkinfer PR #75 "[GG] Add BF16 MLA query projection and
+ * assembly", sections "What" and "Contract"; vLLM PR #174 "[GG] Fuse MXFP8 and
+ * BF16 MLA query assembly", section "What"): for every decode token m < M and
+ * local head h < H,
+ *
+ *   out[m,h,0:512]   = cvt( bf16_rne( sum_k q_nope[m,h,k] * W[h,k,n] ) )   fp32 accumulation
+ *   out[m,h,512:576] = cvt( q_pe[m,h,0:64] )                                same launch, no concat
+ *
+ * where cvt is the identity for BF16 output and x -> e4m3_satfinite(fp32(x) / q_scale)
+ * for E4M3 output, and W is either BF16 or MXFP8 (E4M3 payload times an E8M0
+ * scale 2^(S-127) shared by 32 contiguous latent columns of one k row; the
+ * weight is N-major with its scales along n, per the review thread on api.py
+ * of the sparkinfer page). The summation order over k is unspecified, so the
+ * BF16 projection is not a bitwise contract (sparkinfer page, "Contract").
+ *
+ * Fixed sizes: nope (K) = 128, latent (N) = 512, rope (R) = 64, so each output
+ * row holds 576 elements. Supported plans: H in {8, 11, 16} local heads and
+ * 1 <= M <= 32 tokens (vLLM page, "What" and "Layout and topology
+ * behavior"); anything else is MLAQ_ERR_UNSUPPORTED and the caller keeps its
+ * staged path (vLLM page, "Safety scope and PR 173").
+ *
+ * All entry points are thread-safe. No C++ exception crosses the ABI. Every
+ * buffer is caller-owned device memory; the library keeps no pointer after a
+ * call returns and allocates nothing in mlaq_run.
+ */
+#ifndef MLAQ_H_
+#define MLAQ_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats. */
+#define MLAQ_WEIGHT_BF16 0  /* W_UK_T bf16 [H,128,512], n fastest */
+#define MLAQ_WEIGHT_MXFP8 1 /* E4M3FN payload [H,128,512] + E8M0 scales [H,128,16] */
+
+/* Output element types. */
+#define MLAQ_OUT_BF16 0 /* bf16 [M,H,576] */
+#define MLAQ_OUT_E4M3 1 /* OCP E4M3FN [M,H,576], scaled by 1/q_scale, saturating at +-448 */
+
+/* Status codes. */
+#define MLAQ_OK 0
+#define MLAQ_ERR_UNSUPPORTED 1 /* plan outside the fused path: keep the staged path */
+#define MLAQ_ERR_INVALID_ARG 2 /* bad pointer, alignment, scale presence, overlap or enum */
+#define MLAQ_ERR_DEVICE 3      /* a HIP call failed (device query or launch) */
+
+#define MLAQ_NOPE_DIM 128
+#define MLAQ_LATENT_DIM 512
+#define MLAQ_ROPE_DIM 64
+#define MLAQ_MAX_M 32
+
+/*
+ * mlaq_plan_supported -- the pure capability gate (no HIP call).
+ * Mirrors can_implement(num_heads, max_m, nope_dim, latent_dim, output_dtype,
+ * weight_format, device) of the sparkinfer page (review thread on api.py), with
+ * the device replaced by its architecture name (e.g. "gfx950:sramecc+:xnack-")
+ * and the rope width made explicit. Each weight format has its own gate, so
+ * the BF16 plan does not inherit MXFP8-only requirements (same thread).
+ * Returns MLAQ_OK when the fused path covers the plan, MLAQ_ERR_UNSUPPORTED
+ * when it does not (arch not gfx950, H not in {8,11,16}, max_m outside
+ * 1..32, dims other than 128/512/64), MLAQ_ERR_INVALID_ARG for an unknown
+ * enum or a NULL arch. mlaq_last_error() says which.
+ */
+int mlaq_plan_supported(int num_heads, int max_m, int nope_dim, int latent_dim, int rope_dim,
+                        int weight_format, int out_dtype, const char* arch);
+
+/*
+ * mlaq_can_implement -- 1 when the fused path covers the plan on HIP device
+ * `device` (an ordinal), else 0. Queries the device's architecture once and
+ * caches it; enqueues nothing and never synchronizes.
+ */
+int mlaq_can_implement(int num_heads, int max_m, int nope_dim, int latent_dim, int rope_dim,
+                       int weight_format, int out_dtype, int device);
+
+/*
+ * mlaq_prewarm -- load the kernels that serve the given token counts
+ * (`m_regimes[0..n_regimes)`, each in 1..32) for H heads on `device`, and
+ * cache the device's architecture, so later mlaq_run calls do no first-use
+ * work and can be captured into a hipGraph. Deduplicates regimes that share a
+ * kernel, allocates nothing that outlives the call, may block. Idempotent.
+ * (sparkinfer page, walkthrough: prewarm of weight and M regimes; vLLM page,
+ * "Layout and topology behavior": prewarm only the graph-visible M regimes.)
+ * Returns MLAQ_OK, MLAQ_ERR_UNSUPPORTED, MLAQ_ERR_INVALID_ARG (NULL regimes
+ * with n_regimes > 0, bad enum) or MLAQ_ERR_DEVICE.
+ */
+int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_format,
+                 int out_dtype, int device);
+
+/*
+ * mlaq_run -- enqueue one fused call on `stream` (a hipStream_t passed as
+ * void*; NULL is the null stream) of the current HIP device. Asynchronous:
+ * no host synchronization, no allocation, capturable into a hipGraph; the
+ * kernel reads *q_scale when it runs, so graph replays see new scale values.
+ *
+ *   q_nope   bf16 [M,H,128], contiguous, 16-byte aligned
+ *   q_pe     bf16 [M,H,64], contiguous, 16-byte aligned
+ *   w        bf16 [H,128,512] (MLAQ_WEIGHT_BF16) or E4M3FN bytes [H,128,512]
+ *            (MLAQ_WEIGHT_MXFP8), n fastest, 16-byte aligned
+ *   w_scales E8M0 bytes [H,128,16]: byte [h,k,j] scales columns 32j..32j+31
+ *            of row k; required for MXFP8, must be NULL for BF16 weights
+ *   q_scale  device fp32[1], 4-byte aligned; required for E4M3 output, must be
+ *            NULL for BF16 output (the BF16 output takes no scale)
+ *   out      bf16 or E4M3 [M,H,576], contiguous, 16-byte aligned, must not
+ *            overlap any input
+ *   M        tokens, 0..32 (M = 0 is a no-op that returns MLAQ_OK)
+ *   H        heads, 8, 11 or 16
+ *
+ * MXFP8 weights decode exactly for scale bytes 10..246, where every nonzero
+ * decoded weight is a normal bf16 value (2^-126 <= |w| <= 448 * 2^119);
+ * NaN payload codes propagate.
+ * Results are deterministic: the same inputs give the same bits.
+ * Returns MLAQ_OK, or a non-OK status with `out` untouched and nothing
+ * enqueued; mlaq_last_error() describes it.
+ */
+int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_scales,
+             const float* q_scale, void* out, int M, int H, int weight_format, int out_dtype,
+             void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the thread's next mlaq_* call. */
+const char* mlaq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLAQ_H_ */

@@ -1,0 +1,172 @@
+"""Python binding of libmlaq, the MI355X fused MLA decode query projection.
+
+Argument marshalling only: every step of the operation runs in the HIP
+kernels of ``libmlaq.so`` (built in-tree by ``mla_decode_query_amd._build``).
+PyTorch supplies device memory and the current stream. There is no fallback:
+if the library is missing or a call fails, these functions raise.
+
+The entry points carry the C names (see ``include/mlaq.h``):
+
+* ``mlaq_plan_supported`` -- pure capability gate for an architecture name;
+* ``mlaq_can_implement``  -- the gate for a device (sparkinfer PR #75
+  "[GG] Add BF16 MLA query projection and assembly", review thread on
+  ``api.py``: can_implement with one gate per weight format);
+* ``mlaq_prewarm``        -- load the kernels of the graph-visible M regimes
+  before capture (vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query
+  assembly", "Layout and topology behavior");
+* ``mlaq_run``            -- one fused call: ``[M,H,576]`` output with q_pe
+  appended in the same launch (sparkinfer page, "What"; vLLM page, "What").
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libmlaq.so"
+
+MLAQ_WEIGHT_BF16, MLAQ_WEIGHT_MXFP8 = 0, 1
+MLAQ_OUT_BF16, MLAQ_OUT_E4M3 = 0, 1
+MLAQ_OK, MLAQ_ERR_UNSUPPORTED, MLAQ_ERR_INVALID_ARG, MLAQ_ERR_DEVICE = 0, 1, 2, 3
+NOPE_DIM, LATENT_DIM, ROPE_DIM, MAX_M = 128, 512, 64, 32
+ROW = LATENT_DIM + ROPE_DIM
+MX_BLOCK = 32
+
+_STATUS_NAMES = {0: "MLAQ_OK", 1: "MLAQ_ERR_UNSUPPORTED", 2: "MLAQ_ERR_INVALID_ARG", 3: "MLAQ_ERR_DEVICE"}
+
+
+class MlaqError(RuntimeError):
+    """A non-OK status from libmlaq; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libmlaq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m mla_decode_query_amd._build")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        I, P = ctypes.c_int, ctypes.c_void_p
+        lib.mlaq_plan_supported.argtypes = [I] * 7 + [ctypes.c_char_p]
+        lib.mlaq_plan_supported.restype = I
+        lib.mlaq_can_implement.argtypes = [I] * 8
+        lib.mlaq_can_implement.restype = I
+        lib.mlaq_prewarm.argtypes = [I, P, I, I, I, I]
+        lib.mlaq_prewarm.restype = I
+        lib.mlaq_run.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+        lib.mlaq_run.restype = I
+        lib.mlaq_last_error.argtypes = []
+        lib.mlaq_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def mlaq_last_error() -> str:
+    return library().mlaq_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MLAQ_OK:
+        raise MlaqError(status, mlaq_last_error())
+
+
+def _device_index(device) -> int:
+    if device is None:
+        return torch.cuda.current_device()
+    if isinstance(device, int):
+        return device
+    d = torch.device(device)
+    return d.index if d.index is not None else torch.cuda.current_device()
+
+
+def mlaq_plan_supported(num_heads: int, max_m: int, nope_dim: int = NOPE_DIM, latent_dim: int = LATENT_DIM,
+                        rope_dim: int = ROPE_DIM, weight_format: int = MLAQ_WEIGHT_MXFP8,
+                        out_dtype: int = MLAQ_OUT_BF16, arch: str = "gfx950") -> int:
+    """Status of the pure gate for an architecture name (no HIP call)."""
+    return library().mlaq_plan_supported(num_heads, max_m, nope_dim, latent_dim, rope_dim, weight_format,
+                                         out_dtype, arch.encode() if arch is not None else None)
+
+
+def mlaq_can_implement(num_heads: int, max_m: int, nope_dim: int = NOPE_DIM, latent_dim: int = LATENT_DIM,
+                       rope_dim: int = ROPE_DIM, weight_format: int = MLAQ_WEIGHT_MXFP8,
+                       out_dtype: int = MLAQ_OUT_BF16, device=None) -> bool:
+    """True when the fused path covers the plan on ``device``."""
+    return bool(library().mlaq_can_implement(num_heads, max_m, nope_dim, latent_dim, rope_dim, weight_format,
+                                             out_dtype, _device_index(device)))
+
+
+def mlaq_prewarm(num_heads: int, m_regimes, weight_format: int, out_dtype: int, device=None) -> None:
+    """Load the kernels serving ``m_regimes`` (call before graph capture)."""
+    regs = list(m_regimes)
+    arr = (ctypes.c_int * max(1, len(regs)))(*regs)
+    _check(library().mlaq_prewarm(num_heads, arr, len(regs), weight_format, out_dtype, _device_index(device)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def mlaq_run(q_nope: torch.Tensor, q_pe: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None,
+             q_scale: torch.Tensor | None, out: torch.Tensor, weight_format: int, out_dtype: int,
+             stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue one fused call on ``stream`` (default: the current stream).
+
+    q_nope bf16 [M,H,128]; q_pe bf16 [M,H,64]; w bf16 [H,128,512] or
+    float8_e4m3fn/uint8 [H,128,512]; w_scales uint8/float8_e8m0fnu [H,128,16]
+    (MXFP8) or None; q_scale fp32 [1] (E4M3 output) or None; out bf16 or
+    float8_e4m3fn/uint8 [M,H,576]. Shapes and dtypes are checked here; the
+    library checks pointers, alignment, scale presence and overlap.
+    """
+    M, H = int(q_nope.shape[0]), int(q_nope.shape[1]) if q_nope.dim() == 3 else -1
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", torch.bfloat16, (M, H, NOPE_DIM), dev)
+    _expect(q_pe, "q_pe", torch.bfloat16, (M, H, ROPE_DIM), dev)
+    if weight_format == MLAQ_WEIGHT_BF16:
+        _expect(w, "w", torch.bfloat16, (H, NOPE_DIM, LATENT_DIM), dev)
+    else:
+        _expect(w, "w", w.dtype if w.dtype in (torch.float8_e4m3fn, torch.uint8) else torch.float8_e4m3fn,
+                (H, NOPE_DIM, LATENT_DIM), dev)
+    if w_scales is not None:
+        _expect(w_scales, "w_scales",
+                w_scales.dtype if w_scales.dtype in (torch.uint8, torch.float8_e8m0fnu) else torch.uint8,
+                (H, NOPE_DIM, LATENT_DIM // MX_BLOCK), dev)
+    if q_scale is not None:
+        _expect(q_scale, "q_scale", torch.float32, (1,), dev)
+    odt = torch.bfloat16 if out_dtype == MLAQ_OUT_BF16 else (
+        out.dtype if out.dtype in (torch.float8_e4m3fn, torch.uint8) else torch.float8_e4m3fn)
+    _expect(out, "out", odt, (M, H, ROW), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(library().mlaq_run(_ptr(q_nope), _ptr(q_pe), _ptr(w), _ptr(w_scales), _ptr(q_scale), _ptr(out),
+                              M, H, weight_format, out_dtype, ctypes.c_void_p(s.cuda_stream)))
+
+
+def fused_query(q_nope, q_pe, w, w_scales=None, q_scale=None, out_dtype: int = MLAQ_OUT_BF16, out=None):
+    """Allocate the [M,H,576] output (unless given) and run one fused call."""
+    wf = MLAQ_WEIGHT_BF16 if w.dtype == torch.bfloat16 else MLAQ_WEIGHT_MXFP8
+    M, H = q_nope.shape[0], q_nope.shape[1]
+    if out is None:
+        dt = torch.bfloat16 if out_dtype == MLAQ_OUT_BF16 else torch.float8_e4m3fn
+        out = torch.empty((M, H, ROW), dtype=dt, device=q_nope.device)
+    mlaq_run(q_nope, q_pe, w, w_scales, q_scale, out, wf, out_dtype)
+    return out

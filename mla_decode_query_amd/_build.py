@@ -1,0 +1,62 @@
+"""Builds libmlaq.so in-tree with hipcc for gfx950.
+
+    python -m mla_decode_query_amd._build
+
+Every HIP source is compiled with packed-FP32 code generation switched off
+(``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
+not know the feature, which is harmless.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libmlaq.so"
+SOURCES = [CSRC / "mlaq_kernels.hip", CSRC / "mlaq_api.cpp"]
+HEADERS = [ROOT / "include" / "mlaq.h", CSRC / "mlaq_internal.h"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = Path(rocm) / "bin" / "hipcc"
+    return str(cand) if cand.exists() else "hipcc"
+
+
+def build(out: Path | None = None, extra_flags: list[str] | None = None, quiet: bool = True) -> Path:
+    """Compile every source into one shared library; returns its path."""
+    out = Path(out) if out is not None else LIB
+    tmp = out.with_name(out.name + f".tmp{os.getpid()}")
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{ROOT / 'include'}", f"-I{CSRC}",
+           "-o", str(tmp), *map(str, SOURCES)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+    if not quiet:
+        sys.stderr.write(res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def is_stale(lib: Path = LIB) -> bool:
+    if not lib.exists():
+        return True
+    t = lib.stat().st_mtime
+    return any(p.stat().st_mtime > t for p in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(quiet=False))

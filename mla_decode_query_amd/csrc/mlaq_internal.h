@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI front end (mlaq_api.cpp) and the
+// kernels (mlaq_kernels.hip). Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlaq {
+
+constexpr int kNope = 128;   // K: reduction width
+constexpr int kLatent = 512; // N: projection width
+constexpr int kRope = 64;    // R: appended q_pe width
+constexpr int kRow = kLatent + kRope;
+constexpr int kMxBlock = 32; // E8M0 scale group along n
+constexpr int kMaxM = 32;
+
+// Kernel arguments, passed by value (one kernarg segment).
+struct FusedArgs {
+  const uint16_t* q_nope; // bf16 [M,H,K]
+  const uint16_t* q_pe;   // bf16 [M,H,R]
+  const void* w;          // bf16 or E4M3 [H,K,N]
+  const uint8_t* w_scales; // E8M0 [H,K,N/32] or null
+  const float* q_scale;   // device fp32 or null
+  void* out;              // bf16 or E4M3 [M,H,N+R]
+  int M;
+  int H;
+};
+
+// Identifies one compiled kernel.
+struct Variant {
+  int weight_format; // MLAQ_WEIGHT_*
+  int out_dtype;     // MLAQ_OUT_*
+  int m_tiles;       // 16-token tiles: 1 (M <= 16) or 2 (M <= 32)
+};
+
+inline Variant variant_for(int weight_format, int out_dtype, int M) {
+  return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2};
+}
+
+// Host function pointer of the kernel for a variant (null if none).
+const void* kernel_for(const Variant& v);
+// Launch geometry of a variant for H heads.
+void launch_shape(const Variant& v, int H, dim3* grid, dim3* block);
+
+} // namespace mlaq

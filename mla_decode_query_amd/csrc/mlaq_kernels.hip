@@ -1,0 +1,334 @@
+// mlaq_kernels.hip -- gfx950 kernels of the fused MLA decode query projection
+// and assembly (sparkinfer PR #75 "[GG] Add BF16 MLA query projection and
+// assembly", sections "What" and "Contract"; vLLM PR #174 "[GG] Fuse MXFP8
+// and BF16 MLA query assembly", section "What").
+//
+// One launch computes, for all M tokens and H heads,
+//   out[m,h,0:512]   = cvt(bf16_rne(sum_k q_nope[m,h,k] * W[h,k,n]))
+//   out[m,h,512:576] = cvt(q_pe[m,h,:])
+// with cvt = identity (BF16 output) or e4m3_satfinite(x / q_scale).
+//
+// Decomposition. The call moves ~1-2 MiB of weights and little else, so the
+// kernel is an HBM stream whose cost is latency: every weight byte is
+// requested at kernel entry, spread over as many CUs as the tiling allows.
+// A workgroup (4 waves) owns one head h and one slice of WCOLS = 16*VEC
+// latent columns, over all 128 k. Wave w takes k rows [32w, 32w+32).
+//
+// Contraction on MFMA without any transpose. v_mfma_f32_16x16x32_bf16 pairs
+// element e of lane (i + 16g) of A with element e of lane (j + 16g) of B, for
+// output (i, j). A lane loads VEC consecutive columns of 8 consecutive k rows
+// (the weight is n-major, so each row segment is a coalesced load). For each
+// of its VEC columns it builds a B fragment from those 8 rows (v_perm packs
+// two rows' bf16 into one dword) and issues one MFMA whose output column j is
+// relabelled as latent column c0 + VEC*j + i. The A fragment is the q_nope
+// row of token i over the same 8 k per lane group, loaded straight from
+// global memory. So the 16-wide MFMA column index walks 16 column groups, the
+// 4 lane groups walk the 4 k octets, and no LDS round trip is needed for
+// either operand. M <= 16 uses one 16-token tile, M <= 32 two.
+//
+// The four waves' fp32 partial tiles are summed through LDS in a fixed order
+// (wave 0 + 1 + 2 + 3), so results are deterministic. The epilogue rounds to
+// bf16 (and for E4M3 output divides by q_scale and encodes), and the same
+// workgroups copy q_pe into columns 512..575 of the row.
+//
+// MXFP8 weights are decoded in registers: v_cvt_pk_f32_fp8 gives the exact
+// fp32 value of each E4M3 byte, the product with 2^(S-127) is exact, and the
+// top half of that fp32 is its exact bf16. The bf16 MFMA then forms exact
+// products with q_nope, as the pages' exact dequantization requires.
+#include "mlaq.h"
+#include "mlaq_internal.h"
+
+namespace mlaq {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256; // 4 waves of 64
+constexpr int kScalesPerRow = kLatent / kMxBlock;
+
+// ---------------------------------------------------------------------------
+// Codecs (device side, written from the OCP OFP8 / MX v1.0 definitions)
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest even, every overflow (infinity
+// included) saturating to +-448, NaN -> 0x7f with the sign kept.
+__device__ __forceinline__ uint32_t e4m3_satfinite(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;  // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu; // |v| >= 448
+  if (a >= 0x3c800000u) {                    // 2^-6 <= |v| < 448: normal codes
+    // Keep 3 mantissa bits, round the 20 dropped bits to nearest even. The
+    // code is the fp32 exponent rebased from 127 to 7, then the mantissa.
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t code = (r >> 20) - (120u << 3);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+  }
+  // |v| < 2^-6: subnormal codes are multiples of 2^-9 (code 8 is 2^-6).
+  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+}
+
+// E8M0 scale byte -> 2^(s-127) as fp32 (0xff -> NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : s << 23);
+  return __uint_as_float(bits);
+}
+
+// ---------------------------------------------------------------------------
+// Loads
+// ---------------------------------------------------------------------------
+
+template <int RB>
+__device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[RB / 4]) {
+  if constexpr (RB == 4) {
+    d[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (RB == 8) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    d[0] = v[0];
+    d[1] = v[1];
+  } else {
+    static_assert(RB == 16, "row segment must be 4, 8 or 16 bytes");
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    d[0] = v[0];
+    d[1] = v[1];
+    d[2] = v[2];
+    d[3] = v[3];
+  }
+}
+
+// Block -> tile. When a tile's row segment is shorter than a 128-byte line,
+// the two tiles sharing each line are given blocks b and b+8, which the
+// dispatcher places on the same XCD (round-robin over 8), so the line is
+// fetched into one L2 only. A trailing group of fewer than 16 blocks keeps
+// the identity mapping.
+__device__ __forceinline__ int tile_of_block(int b, int nblocks, bool pair) {
+  if (!pair) return b;
+  const int grp = b >> 4;
+  if ((grp << 4) + 16 > nblocks) return b;
+  const int y = b & 15;
+  return (grp << 4) + 2 * (y & 7) + (y >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// The fused kernel
+// ---------------------------------------------------------------------------
+
+template <int WF, int OF, int MT, int VEC>
+__global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
+  constexpr int ESZ = (WF == MLAQ_WEIGHT_BF16) ? 2 : 1; // bytes per weight
+  constexpr int WCOLS = 16 * VEC;                       // latent columns per workgroup
+  constexpr int NCT = kLatent / WCOLS;                  // column tiles per head
+  constexpr int RB = VEC * ESZ;                         // bytes per lane per k row
+  constexpr int D = RB / 4;                             // dwords per lane per k row
+  constexpr bool PAIR = WCOLS * ESZ < 128;
+  constexpr int MROWS = 16 * MT;
+  constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
+  static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
+  static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 4 == 0, "E4M3 columns come in dword quads");
+  __shared__ float part[4 * MROWS * LDW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int tile = tile_of_block(blockIdx.x, gridDim.x, PAIR);
+  const int h = tile / NCT, ct = tile - h * NCT;
+  const int c0 = ct * WCOLS;
+  const int H = a.H, M = a.M;
+  const int k0 = 32 * wave + 8 * g; // first of this lane's 8 k rows
+  const int col = c0 + VEC * j;     // first of this lane's VEC columns
+
+  // 1. Weight rows (the bulk of the bytes), all requested up front.
+  uint32_t wr[8][D];
+  {
+    const uint8_t* base =
+        static_cast<const uint8_t*>(a.w) + ((size_t(h) * kNope + k0) * kLatent + col) * ESZ;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_row<RB>(base + size_t(r) * kLatent * ESZ, wr[r]);
+  }
+  uint32_t sc[8];
+  if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
+    const uint8_t* sb = a.w_scales + (size_t(h) * kNope + k0) * kScalesPerRow + col / kMxBlock;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sc[r] = sb[r * kScalesPerRow];
+  }
+
+  // 2. q_nope A fragments: token 16t + j, k rows k0..k0+7.
+  u32x4_t qa[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + j;
+    qa[t] = u32x4_t{0u, 0u, 0u, 0u};
+    if (m < M)
+      qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + (size_t(m) * H + h) * kNope + k0);
+  }
+
+  // 3. This thread's q_pe chunk (8 elements): chunk x of the head goes to
+  //    column tile x % NCT, thread x / NCT.
+  const int pe_chunk = ct + NCT * tid;
+  const bool has_pe = pe_chunk < M * (kRope / 8);
+  u32x4_t pe_v = u32x4_t{0u, 0u, 0u, 0u};
+  const int pe_m = pe_chunk >> 3, pe_c = pe_chunk & 7;
+  if (has_pe)
+    pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + (size_t(pe_m) * H + h) * kRope + 8 * pe_c);
+
+  float qs = 1.0f;
+  if constexpr (OF == MLAQ_OUT_E4M3) qs = *a.q_scale;
+
+  // 4. Contraction over this wave's 32 k rows.
+  f32x4_t acc[MT][VEC];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (WF == MLAQ_WEIGHT_BF16) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      u32x4_t b;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        b[p] = __builtin_amdgcn_perm(wr[2 * p + 1][i >> 1], wr[2 * p][i >> 1], sel);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
+    }
+  } else {
+    // Exact decode: fp32(E4M3) * 2^(S-127), whose top 16 bits are its bf16.
+    uint32_t wf[8][VEC];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float s = e8m0_scale(sc[r]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(wr[r][d]), false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(wr[r][d]), true);
+        wf[r][4 * d + 0] = __float_as_uint(lo[0] * s);
+        wf[r][4 * d + 1] = __float_as_uint(lo[1] * s);
+        wf[r][4 * d + 2] = __float_as_uint(hi[0] * s);
+        wf[r][4 * d + 3] = __float_as_uint(hi[1] * s);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      u32x4_t b;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wf[2 * p + 1][i], wf[2 * p][i], 0x07060302u);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
+    }
+  }
+
+  // 5. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
+  //    columns VEC*j + i.
+  {
+    float* pw = part + wave * MROWS * LDW;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = pw + (16 * t + 4 * g + r) * LDW + VEC * j;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dst[i] = acc[t][i][r];
+      }
+  }
+  __syncthreads();
+
+  // 6. Epilogue: sum the four k slices, round, convert, store 8 columns.
+  constexpr int GPR = WCOLS / 8;
+  for (int x = tid; x < M * GPR; x += kThreads) {
+    const int m = x / GPR, cg = x - m * GPR;
+    float s[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int off = m * LDW + 8 * cg + c;
+      s[c] = ((part[off] + part[MROWS * LDW + off]) + part[2 * MROWS * LDW + off]) +
+             part[3 * MROWS * LDW + off];
+    }
+    const size_t o = (size_t(m) * H + h) * kRow + c0 + 8 * cg;
+    if constexpr (OF == MLAQ_OUT_BF16) {
+      u32x4_t v;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) v[p] = bf16_rne(s[2 * p]) | (bf16_rne(s[2 * p + 1]) << 16);
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = v;
+    } else {
+      u32x2_t v = u32x2_t{0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float y = __uint_as_float(bf16_rne(s[c]) << 16);
+        v[c >> 2] |= e4m3_satfinite(y / qs) << (8 * (c & 3));
+      }
+      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
+    }
+  }
+
+  // 7. q_pe into columns 512..575 of the same row.
+  if (has_pe) {
+    const size_t o = (size_t(pe_m) * H + h) * kRow + kLatent + 8 * pe_c;
+    if constexpr (OF == MLAQ_OUT_BF16) {
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = pe_v;
+    } else {
+      u32x2_t v = u32x2_t{0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float x = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
+        v[c >> 2] |= e4m3_satfinite(x / qs) << (8 * (c & 3));
+      }
+      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
+    }
+  }
+}
+
+// Columns per lane per k row for each weight format: 4-byte row segments,
+// i.e. 32 (bf16) or 64 (E4M3) columns per workgroup.
+template <int WF>
+constexpr int vec_of() {
+  return WF == MLAQ_WEIGHT_BF16 ? 2 : 4;
+}
+
+template <int WF, int OF, int MT>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF>()>);
+}
+
+} // namespace
+
+const void* kernel_for(const Variant& v) {
+#define MLAQ_CASE(WF, OF, MT)                                              \
+  if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT) \
+    return kernel_ptr<WF, OF, MT>();
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1)
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 2)
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 1)
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 2)
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 1)
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 2)
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 1)
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 2)
+#undef MLAQ_CASE
+  return nullptr;
+}
+
+void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
+  const int vec = v.weight_format == MLAQ_WEIGHT_BF16 ? vec_of<MLAQ_WEIGHT_BF16>() : vec_of<MLAQ_WEIGHT_MXFP8>();
+  *grid = dim3(unsigned(H * (kLatent / (16 * vec))), 1, 1);
+  *block = dim3(kThreads, 1, 1);
+}
+
+} // namespace mlaq
