@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off",
     "-Wall",
 ]
 

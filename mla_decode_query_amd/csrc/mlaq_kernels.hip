@@ -54,31 +54,43 @@ constexpr int kScalesPerRow = kLatent / kMxBlock;
 // Codecs (device side, written from the OCP OFP8 / MX v1.0 definitions)
 // ---------------------------------------------------------------------------
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> packed bf16 (low half = lo), round to nearest even, NaN kept
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// fp32 -> OCP E4M3FN code, round to nearest even, every overflow (infinity
-// included) saturating to +-448, NaN -> 0x7f with the sign kept.
-__device__ __forceinline__ uint32_t e4m3_satfinite(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7fu;  // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu; // |v| >= 448
-  if (a >= 0x3c800000u) {                    // 2^-6 <= |v| < 448: normal codes
-    // Keep 3 mantissa bits, round the 20 dropped bits to nearest even. The
-    // code is the fp32 exponent rebased from 127 to 7, then the mantissa.
-    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-    const uint32_t code = (r >> 20) - (120u << 3);
-    return sign | (code > 0x7eu ? 0x7eu : code);
-  }
-  // |v| < 2^-6: subnormal codes are multiples of 2^-9 (code 8 is 2^-6).
-  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+// The E4M3 conversion saturates: every finite or infinite value past 448 is
+// 448 (NaN stays NaN). v_cvt_pk_fp8_f32 rounds to nearest even into OCP
+// E4M3FN but turns out-of-range values into NaN, hence the clamp.
+__device__ __forceinline__ float clamp448(float v) {
+  return __builtin_isnan(v) ? v : __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+}
+
+// Four fp32 -> four OCP E4M3FN codes (byte c holds value c), round to nearest
+// even, saturating to +-448.
+__device__ __forceinline__ uint32_t e4m3x4_satfinite(float v0, float v1, float v2, float v3) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v0), clamp448(v1), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v2), clamp448(v3), r, true);
+  return uint32_t(r);
+}
+
+// Correctly rounded fp32 quotient y / b from rb = RN(1/b): q0 = RN(y * rb)
+// is within one ulp of y / b, the residual y - q0 * b is exact in one FMA,
+// and one FMA correction then gives RN(y / b) (Markstein's correction step).
+// Checked against IEEE division for every finite bf16 y and 40,000 divisors
+// with 2^-64 <= |b| < 2^65. For |y| < 2^-100 the residual can underflow; such
+// quotients are far below the smallest E4M3 step, and q0 carries their sign.
+__device__ __forceinline__ float div_rn(float y, float b, float rb) {
+  const float q0 = y * rb;
+  const float rho = __builtin_fmaf(-q0, b, y);
+  const float q1 = __builtin_fmaf(rho, rb, q0);
+  // q0 is the answer when it is not finite (overflow, NaN) and for tiny or
+  // zero y (which also keeps the sign of a zero quotient).
+  const bool plain = !(__builtin_fabsf(y) >= 0x1p-100f) || !(__builtin_fabsf(q0) <= 0x1.fffffep127f);
+  return plain ? q0 : q1;
 }
 
 // E8M0 scale byte -> 2^(s-127) as fp32 (0xff -> NaN).
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
   static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
   static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 4 == 0, "E4M3 columns come in dword quads");
-  __shared__ float part[4 * MROWS * LDW];
+  __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -150,7 +162,17 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   const int k0 = 32 * wave + 8 * g; // first of this lane's 8 k rows
   const int col = c0 + VEC * j;     // first of this lane's VEC columns
 
-  // 1. Weight rows (the bulk of the bytes), all requested up front.
+  // 1. This thread's q_pe chunk (8 elements), requested first so that its
+  //    store can leave while the weights are still in flight. Chunk x of the
+  //    head goes to column tile x % NCT, thread x / NCT.
+  const int pe_chunk = ct + NCT * tid;
+  const bool has_pe = pe_chunk < M * (kRope / 8);
+  const int pe_x = has_pe ? pe_chunk : 0; // loads stay unconditional (no branch, no early wait)
+  const int pe_m = pe_x >> 3, pe_c = pe_x & 7;
+  const u32x4_t pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + (size_t(pe_m) * H + h) * kRope + 8 * pe_c);
+  __builtin_amdgcn_sched_barrier(0); // keep the q_pe load ahead of the weight loads
+
+  // 2. Weight rows (the bulk of the bytes), all requested up front.
   uint32_t wr[8][D];
   {
     const uint8_t* base =
@@ -165,29 +187,45 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
     for (int r = 0; r < 8; ++r) sc[r] = sb[r * kScalesPerRow];
   }
 
-  // 2. q_nope A fragments: token 16t + j, k rows k0..k0+7.
+  // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7.
   u32x4_t qa[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + j;
-    qa[t] = u32x4_t{0u, 0u, 0u, 0u};
-    if (m < M)
-      qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + (size_t(m) * H + h) * kNope + k0);
+    const int mc = m < M ? m : 0; // rows past M read token 0 and are zeroed below
+    qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + (size_t(mc) * H + h) * kNope + k0);
   }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    if (16 * t + j >= M) qa[t] = u32x4_t{0u, 0u, 0u, 0u};
 
-  // 3. This thread's q_pe chunk (8 elements): chunk x of the head goes to
-  //    column tile x % NCT, thread x / NCT.
-  const int pe_chunk = ct + NCT * tid;
-  const bool has_pe = pe_chunk < M * (kRope / 8);
-  u32x4_t pe_v = u32x4_t{0u, 0u, 0u, 0u};
-  const int pe_m = pe_chunk >> 3, pe_c = pe_chunk & 7;
-  if (has_pe)
-    pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + (size_t(pe_m) * H + h) * kRope + 8 * pe_c);
+  __builtin_amdgcn_sched_barrier(0); // all loads are in flight before any wait
 
-  float qs = 1.0f;
-  if constexpr (OF == MLAQ_OUT_E4M3) qs = *a.q_scale;
+  // 4. q_pe into columns 512..575 of its row (a bit copy, or the E4M3
+  //    conversion with the same per-tensor q_scale).
+  float qs = 1.0f, rqs = 1.0f;
+  if constexpr (OF == MLAQ_OUT_E4M3) {
+    qs = *a.q_scale;
+    rqs = 1.0f / qs;
+  }
+  if (has_pe) {
+    const size_t o = (size_t(pe_m) * H + h) * kRow + kLatent + 8 * pe_c;
+    if constexpr (OF == MLAQ_OUT_BF16) {
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = pe_v;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        x[c] = div_rn(__uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16), qs, rqs);
+      u32x2_t v;
+      v[0] = e4m3x4_satfinite(x[0], x[1], x[2], x[3]);
+      v[1] = e4m3x4_satfinite(x[4], x[5], x[6], x[7]);
+      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
 
-  // 4. Contraction over this wave's 32 k rows.
+  // 5. Contraction over this wave's 32 k rows.
   f32x4_t acc[MT][VEC];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -235,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
     }
   }
 
-  // 5. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
+  // 5b. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
   //    columns VEC*j + i.
   {
     float* pw = part + wave * MROWS * LDW;
@@ -250,47 +288,27 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // 6. Epilogue: sum the four k slices, round, convert, store 8 columns.
-  constexpr int GPR = WCOLS / 8;
+  // 6. Epilogue: sum the four k slices in a fixed order, round, convert and
+  //    store; each thread finishes 4 consecutive columns of one token.
+  constexpr int GPR = WCOLS / 4;
   for (int x = tid; x < M * GPR; x += kThreads) {
     const int m = x / GPR, cg = x - m * GPR;
-    float s[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int off = m * LDW + 8 * cg + c;
-      s[c] = ((part[off] + part[MROWS * LDW + off]) + part[2 * MROWS * LDW + off]) +
-             part[3 * MROWS * LDW + off];
-    }
-    const size_t o = (size_t(m) * H + h) * kRow + c0 + 8 * cg;
+    const int off = m * LDW + 4 * cg;
+    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(part + off);
+    const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(part + MROWS * LDW + off);
+    const f32x4_t p2 = *reinterpret_cast<const f32x4_t*>(part + 2 * MROWS * LDW + off);
+    const f32x4_t p3 = *reinterpret_cast<const f32x4_t*>(part + 3 * MROWS * LDW + off);
+    const f32x4_t sum = ((p0 + p1) + p2) + p3;
+    const size_t o = (size_t(m) * H + h) * kRow + c0 + 4 * cg;
+    const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
+    const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
     if constexpr (OF == MLAQ_OUT_BF16) {
-      u32x4_t v;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) v[p] = bf16_rne(s[2 * p]) | (bf16_rne(s[2 * p + 1]) << 16);
-      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = v;
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + o) = u32x2_t{b01, b23};
     } else {
-      u32x2_t v = u32x2_t{0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float y = __uint_as_float(bf16_rne(s[c]) << 16);
-        v[c >> 2] |= e4m3_satfinite(y / qs) << (8 * (c & 3));
-      }
-      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
-    }
-  }
-
-  // 7. q_pe into columns 512..575 of the same row.
-  if (has_pe) {
-    const size_t o = (size_t(pe_m) * H + h) * kRow + kLatent + 8 * pe_c;
-    if constexpr (OF == MLAQ_OUT_BF16) {
-      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = pe_v;
-    } else {
-      u32x2_t v = u32x2_t{0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float x = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
-        v[c >> 2] |= e4m3_satfinite(x / qs) << (8 * (c & 3));
-      }
-      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
+      const float y0 = __uint_as_float(b01 << 16), y1 = __uint_as_float(b01 & 0xffff0000u);
+      const float y2 = __uint_as_float(b23 << 16), y3 = __uint_as_float(b23 & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.out) + o) =
+          e4m3x4_satfinite(div_rn(y0, qs, rqs), div_rn(y1, qs, rqs), div_rn(y2, qs, rqs), div_rn(y3, qs, rqs));
     }
   }
 }
