@@ -58,7 +58,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU-baseline sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device copy (reference for the HBM byte counters) and exit")
     return p.parse_args()
 
 
@@ -197,10 +199,57 @@ def decode_step_leg(torch, mq, wl, args):
     log(f"[bench] staged step: {staged_ms * 1e3:.2f} us/step ({staged_ms / ms:.2f}x fused)")
     del staged_graphs, staged_w, tmp_out, wbf
     torch.cuda.synchronize()
+    floors = floors_leg(torch, mq, layers, copies, stream, args)
     return {
         "layers": layers, "ms": ms, "step_bytes": step_bytes, "dom_ms": dom_ms, "dom_bytes": dom_bytes,
-        "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes,
+        "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes, "floors": floors,
     }
+
+
+def floors_leg(torch, mq, layers, copies, stream, args):
+    """Per-node floors of the launch shape in the same graph loop as the
+    dominant kernel: an empty kernel (256 blocks x 256 threads) and a pure
+    read of each BF16 layer's 2 MiB weight slab (256 blocks, 8 KiB each, the
+    same cold rotation, no compute, no store)."""
+    import ctypes
+
+    path = ROOT / "mla_decode_query_amd" / "libmlaq_diag.so"
+    if not path.exists():
+        log("[bench] libmlaq_diag.so missing: floors skipped")
+        return None
+    diag = ctypes.CDLL(str(path))
+    diag.mlaqdiag_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    diag.mlaqdiag_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                body(torch.cuda.current_stream().cuda_stream)
+        return g
+
+    def empty_body(st):
+        for _ in bf:
+            assert diag.mlaqdiag_empty(256, sink.data_ptr(), st) == 0
+
+    def read_body_for(c):
+        def body(st):
+            for i in bf:
+                w = copies[c][i][0]
+                assert diag.mlaqdiag_stream_read(w.data_ptr(), w.numel() * w.element_size(), sink.data_ptr(), st) == 0
+        return body
+
+    torch.cuda.synchronize()
+    g_empty = [capture(empty_body)]
+    g_read = [capture(read_body_for(c)) for c in range(COPIES)]
+    torch.cuda.synchronize()
+    empty_us = time_graphs(torch, g_empty, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
+    read_us = time_graphs(torch, g_read, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
+    log(f"[bench] floors: empty kernel {empty_us:.3f} us/node, cold 2 MiB stream read {read_us:.3f} us/node")
+    return {"empty_kernel_us": round(empty_us, 4), "cold_read_2MiB_us": round(read_us, 4),
+            "note": "per graph node, same grid as the dominant kernel; the read kernel moves the same weight bytes"}
 
 
 def per_call_leg(torch, mq, wl, reps=100, replays=20):
@@ -242,23 +291,26 @@ def per_call_leg(torch, mq, wl, reps=100, replays=20):
 
 
 def cpu_baseline_leg(wl, layers, budget_s):
-    """The CPU oracle on the step's layers, until the time budget is spent."""
+    """The CPU oracle on the step's layers, cycling through them until the
+    time budget is spent (the oracle as it stands, threaded over heads)."""
     import oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    done_bytes, t_used, n = 0, 0.0, 0
+    host = []
     for idx in range(LAYERS):
         wf = 0 if idx % 2 == 0 else 1
         inp = wl.make_inputs(wl.SEED["c4"] * 100 + idx, H=H, weight_format=wf, M_draw=M_STEP)
         qs = float(layers[idx].qs.item()) if layers is not None else 1.0
+        host.append((wf, inp, qs))
+    done_bytes, t_used, n = 0, 0.0, 0
+    while t_used < budget_s:
+        wf, inp, qs = host[n % LAYERS]
         t0 = time.perf_counter()
         oracle.mla_query(inp.q_nope, inp.q_pe, inp.w, inp.w_scales, qs, weight_format=wf, out_dtype=1,
                          threads=threads, diagnostics=False)
         t_used += time.perf_counter() - t0
         done_bytes += wl.algorithmic_bytes(M_STEP, H, wf, 1)
         n += 1
-        if t_used >= budget_s:
-            break
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -268,9 +320,26 @@ def cpu_baseline_leg(wl, layers, budget_s):
     except OSError:
         pass
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {LAYERS} decode-step layers (H=16, M=32, E4M3 out, BF16/MXFP8 alternating), "
+            "sample": f"{n} layer calls cycling over the {LAYERS} decode-step layers (H=16, M=32, E4M3 out, "
+                      f"BF16/MXFP8 alternating), "
                       f"{t_used:.1f} s with {threads} threads on {cpu} (nproc {os.cpu_count()}); "
-                      f"{t_used / n * 1e3:.1f} ms per layer vs GPU"}
+                      f"{t_used / n * 1e3:.2f} ms per layer"}
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the recorded PMC runs,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+
+    rec = ROOT / "profiles" / "fused_query_decode_step_traffic.txt"
+    if not rec.exists():
+        return None
+    kv = dict(line.split(None, 1) for line in rec.read_text().splitlines() if line and not line.startswith("#"))
+    csrc = ROOT / "mla_decode_query_amd" / "csrc"
+    h = hashlib.sha256((csrc / "mlaq_kernels.hip").read_bytes() + (csrc / "mlaq_internal.h").read_bytes())
+    if h.hexdigest() != kv.get("kernel_source_sha256", "").strip():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def main():
@@ -291,6 +360,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # Reference for the HBM byte counters: one plain device-to-device copy
+        # of exactly 256 MiB (read 256 MiB, write 256 MiB), larger than the
+        # Infinity Cache, after a warm-up copy of the same buffers.
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        return
     log(f"[bench] device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
     step = decode_step_leg(torch, mq, wl, args)
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
@@ -320,10 +402,11 @@ def main():
                    "bytes_per_step": step["step_bytes"]},
         "us_per_layer": round(ms * 1e3 / LAYERS, 4),
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles>",
                      "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"]},
         "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3)},
+        "floors": step["floors"],
         "per_call": per_call,
         "cpu_baseline": cpu,
     }

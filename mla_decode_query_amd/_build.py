@@ -19,6 +19,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libmlaq.so"
 SOURCES = [CSRC / "mlaq_kernels.hip", CSRC / "mlaq_api.cpp"]
+# Measurement floors used by bench.py (not part of the fused path).
+DIAG_LIB = PKG / "libmlaq_diag.so"
+DIAG_SOURCES = [CSRC / "mlaq_diag.hip"]
 HEADERS = [ROOT / "include" / "mlaq.h", CSRC / "mlaq_internal.h"]
 ARCH = "gfx950"
 
@@ -35,12 +38,14 @@ def hipcc() -> str:
     return str(cand) if cand.exists() else "hipcc"
 
 
-def build(out: Path | None = None, extra_flags: list[str] | None = None, quiet: bool = True) -> Path:
-    """Compile every source into one shared library; returns its path."""
+def build(out: Path | None = None, extra_flags: list[str] | None = None, quiet: bool = True,
+          sources: list[Path] | None = None) -> Path:
+    """Compile the sources (default: the fused-path library) into one shared
+    library; returns its path."""
     out = Path(out) if out is not None else LIB
     tmp = out.with_name(out.name + f".tmp{os.getpid()}")
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{ROOT / 'include'}", f"-I{CSRC}",
-           "-o", str(tmp), *map(str, SOURCES)]
+           "-o", str(tmp), *map(str, sources or SOURCES)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
@@ -51,6 +56,11 @@ def build(out: Path | None = None, extra_flags: list[str] | None = None, quiet: 
     return out
 
 
+def build_all(quiet: bool = True) -> list[Path]:
+    """The fused-path library and the benchmark's floor library."""
+    return [build(quiet=quiet), build(DIAG_LIB, quiet=quiet, sources=DIAG_SOURCES)]
+
+
 def is_stale(lib: Path = LIB) -> bool:
     if not lib.exists():
         return True
@@ -59,4 +69,5 @@ def is_stale(lib: Path = LIB) -> bool:
 
 
 if __name__ == "__main__":
-    print(build(quiet=False))
+    for p in build_all(quiet=False):
+        print(p)

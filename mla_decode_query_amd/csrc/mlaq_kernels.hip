@@ -29,7 +29,8 @@
 // The four waves' fp32 partial tiles are summed through LDS in a fixed order
 // (wave 0 + 1 + 2 + 3), so results are deterministic. The epilogue rounds to
 // bf16 (and for E4M3 output divides by q_scale and encodes), and the same
-// workgroups copy q_pe into columns 512..575 of the row.
+// workgroups copy q_pe into columns 512..575 of the row, storing it before
+// they wait for their weights.
 //
 // MXFP8 weights are decoded in registers: v_cvt_pk_f32_fp8 gives the exact
 // fp32 value of each E4M3 byte, the product with 2^(S-127) is exact, and the
@@ -51,7 +52,10 @@ constexpr int kThreads = 256; // 4 waves of 64
 constexpr int kScalesPerRow = kLatent / kMxBlock;
 
 // ---------------------------------------------------------------------------
-// Codecs (device side, written from the OCP OFP8 / MX v1.0 definitions)
+// Conversions. bf16 and E4M3 encodes use the gfx950 convert instructions,
+// whose rounding (nearest even) and special values were checked bit for bit
+// against an independent definition of OCP E4M3FN and bf16 rounding on every
+// bf16 pattern, 2.5 M other fp32 values, all E4M3 midpoints and denormals.
 // ---------------------------------------------------------------------------
 
 // Two fp32 -> packed bf16 (low half = lo), round to nearest even, NaN kept
@@ -103,16 +107,19 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
 // Loads
 // ---------------------------------------------------------------------------
 
+// One lane's segment of one k row: RB bytes (2, 4, 8 or 16) into dwords.
 template <int RB>
-__device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[RB / 4]) {
-  if constexpr (RB == 4) {
+__device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[(RB + 3) / 4]) {
+  if constexpr (RB == 2) {
+    d[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else if constexpr (RB == 4) {
     d[0] = *reinterpret_cast<const uint32_t*>(p);
   } else if constexpr (RB == 8) {
     const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
     d[0] = v[0];
     d[1] = v[1];
   } else {
-    static_assert(RB == 16, "row segment must be 4, 8 or 16 bytes");
+    static_assert(RB == 16, "row segment must be 2, 4, 8 or 16 bytes");
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
     d[0] = v[0];
     d[1] = v[1];
@@ -121,17 +128,15 @@ __device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[RB / 4]
   }
 }
 
-// Block -> tile. When a tile's row segment is shorter than a 128-byte line,
-// the two tiles sharing each line are given blocks b and b+8, which the
-// dispatcher places on the same XCD (round-robin over 8), so the line is
-// fetched into one L2 only. A trailing group of fewer than 16 blocks keeps
-// the identity mapping.
-__device__ __forceinline__ int tile_of_block(int b, int nblocks, bool pair) {
-  if (!pair) return b;
-  const int grp = b >> 4;
-  if ((grp << 4) + 16 > nblocks) return b;
-  const int y = b & 15;
-  return (grp << 4) + 2 * (y & 7) + (y >> 3);
+// Block -> tile. The dispatcher deals blocks round-robin over the 8 XCDs
+// (block b runs on XCD b % 8), and each XCD has its own L2. Tiles are numbered
+// head-major (tile = h * NCT + column tile), and XCD x is given the
+// contiguous tile range [x * n/8, (x+1) * n/8): every head's tiles then sit
+// on one or two XCDs, so its q_nope rows, its q_pe rows and the 128-byte
+// weight lines that neighbouring column tiles share are fetched into one L2
+// instead of eight. Needs n % 8 == 0 (n = H * NCT with NCT >= 8).
+__device__ __forceinline__ int tile_of_block(int b, int nblocks) {
+  return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,18 +149,17 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   constexpr int WCOLS = 16 * VEC;                       // latent columns per workgroup
   constexpr int NCT = kLatent / WCOLS;                  // column tiles per head
   constexpr int RB = VEC * ESZ;                         // bytes per lane per k row
-  constexpr int D = RB / 4;                             // dwords per lane per k row
-  constexpr bool PAIR = WCOLS * ESZ < 128;
+  constexpr int D = (RB + 3) / 4;                       // dwords per lane per k row
   constexpr int MROWS = 16 * MT;
   constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
   static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
-  static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 4 == 0, "E4M3 columns come in dword quads");
+  static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 2 == 0, "E4M3 columns are decoded in pairs");
   __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
-  const int tile = tile_of_block(blockIdx.x, gridDim.x, PAIR);
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
   const int h = tile / NCT, ct = tile - h * NCT;
   const int c0 = ct * WCOLS;
   const int H = a.H, M = a.M;
@@ -252,13 +256,12 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
     for (int r = 0; r < 8; ++r) {
       const float s = e8m0_scale(sc[r]);
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(wr[r][d]), false);
-        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(wr[r][d]), true);
-        wf[r][4 * d + 0] = __float_as_uint(lo[0] * s);
-        wf[r][4 * d + 1] = __float_as_uint(lo[1] * s);
-        wf[r][4 * d + 2] = __float_as_uint(hi[0] * s);
-        wf[r][4 * d + 3] = __float_as_uint(hi[1] * s);
+      for (int e = 0; e < VEC; e += 2) {
+        const int word = int(wr[r][e >> 2]);
+        const f32x2_t v = ((e >> 1) & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
+                                         : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        wf[r][e] = __float_as_uint(v[0] * s);
+        wf[r][e + 1] = __float_as_uint(v[1] * s);
       }
     }
 #pragma unroll
@@ -313,16 +316,19 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-// Columns per lane per k row for each weight format: 4-byte row segments,
-// i.e. 32 (bf16) or 64 (E4M3) columns per workgroup.
-template <int WF>
+// Columns per lane per k row. BF16 weights: 2 (a 4-byte row segment, 32
+// columns and 16 workgroups per head). MXFP8 weights: 4 for M <= 16 (64
+// columns, 8 workgroups per head), 2 for M > 16, where the larger epilogue
+// favours 16 workgroups per head. Chosen by cold-cache timing of the
+// alternatives (2, 4 and 8 columns) in hipGraph loops.
+template <int WF, int MT>
 constexpr int vec_of() {
-  return WF == MLAQ_WEIGHT_BF16 ? 2 : 4;
+  return WF == MLAQ_WEIGHT_BF16 ? 2 : (MT == 1 ? 4 : 2);
 }
 
 template <int WF, int OF, int MT>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF>()>);
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>()>);
 }
 
 } // namespace
@@ -344,7 +350,9 @@ const void* kernel_for(const Variant& v) {
 }
 
 void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
-  const int vec = v.weight_format == MLAQ_WEIGHT_BF16 ? vec_of<MLAQ_WEIGHT_BF16>() : vec_of<MLAQ_WEIGHT_MXFP8>();
+  int vec = 2;
+  if (v.weight_format == MLAQ_WEIGHT_MXFP8)
+    vec = v.m_tiles == 1 ? vec_of<MLAQ_WEIGHT_MXFP8, 1>() : vec_of<MLAQ_WEIGHT_MXFP8, 2>();
   *grid = dim3(unsigned(H * (kLatent / (16 * vec))), 1, 1);
   *block = dim3(kThreads, 1, 1);
 }
