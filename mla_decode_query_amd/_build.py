@@ -4,7 +4,9 @@
 
 Every HIP source is compiled with packed-FP32 code generation switched off
 (``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
-not know the feature, which is harmless.
+not know the feature, which is harmless. ``-ffp-contract=off`` keeps every
+multiply and add as written (the epilogue's division correction relies on
+explicit FMAs only).
 """
 
 from __future__ import annotations
@@ -28,6 +30,9 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off",
+    # MFMA accumulators in ordinary VGPRs (gfx90a+ form): saves the AGPR read-back
+    # of every partial tile before the LDS reduction.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

@@ -191,18 +191,16 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
     for (int r = 0; r < 8; ++r) sc[r] = sb[r * kScalesPerRow];
   }
 
-  // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7.
+  // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7. Rows past M read
+  //    token 0 instead; MFMA output row i depends only on A row i, and rows
+  //    past M are never stored, so they need no zeroing.
   u32x4_t qa[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + j;
-    const int mc = m < M ? m : 0; // rows past M read token 0 and are zeroed below
+    const int mc = m < M ? m : 0;
     qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + (size_t(mc) * H + h) * kNope + k0);
   }
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-    if (16 * t + j >= M) qa[t] = u32x4_t{0u, 0u, 0u, 0u};
-
   __builtin_amdgcn_sched_barrier(0); // all loads are in flight before any wait
 
   // 4. q_pe into columns 512..575 of its row (a bit copy, or the E4M3
