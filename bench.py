@@ -22,6 +22,9 @@ Printed JSON line (stdout, one line):
               against the 8 TB/s HBM peak
   per_call    warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
               MXFP8 weights (BF16 output), with the staged torch baseline
+  pages_shape the pages' own workload (K=192, H=8, M=1, BF16, 78 layers,
+              cold) fused vs staged per layer, and their AB/BA graph-replay
+              comparison over H=8/11/16 x M=1/4/32
   staged      the staged path (torch.bmm + copies + E4M3 quantization) of the
               same step on the same GPU
   cpu_baseline the CPU oracle timed on this host over a bounded sample of the
@@ -58,6 +61,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true")
+    p.add_argument("--no-pages-shape", action="store_true")
+    p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters) and exit")
@@ -290,6 +295,107 @@ def per_call_leg(torch, mq, wl, reps=100, replays=20):
     return res
 
 
+def pages_shape_leg(torch, mq, wl, args):
+    """The pages' own workload: GLM query absorption, nope width 192, TP8 (H=8
+    heads per rank), one decode token, BF16 W_UK_T and output, 78 layers per
+    decode step (sparkinfer PR #75 "[GG] Add BF16 MLA query projection and
+    assembly", "What" and "Performance evidence"; vLLM PR #174, "Performance
+    evidence": 2.88 us fused vs 4.05 us staged per layer on SM12x GPUs,
+    context only). Cold weights (4 rotated copies of 78 distinct layers,
+    468 MiB). Also the pages' standalone graph-replay comparison: one fused
+    call vs the staged bmm + concat, 1,000 balanced AB/BA samples per shape,
+    H = 8/11/16 x M = 1/4/32, median ratio fused/staged."""
+    K, H8, M1, L, C = 192, 8, 1, 78, 4
+    stream = torch.cuda.Stream()
+    lay = []
+    for l in range(L):
+        inp = wl.make_inputs(wl.SEED["c0"] * 100 + l, H=H8, weight_format=mq.MLAQ_WEIGHT_BF16, M_draw=M1, K=K)
+        q_hm = dev_bf16(torch, np.ascontiguousarray(inp.q_nope.transpose(1, 0, 2)))  # [H,M,K] batch view
+        lay.append({"q_hm": q_hm, "pe": dev_bf16(torch, inp.q_pe), "w_host": inp.w,
+                    "out": torch.empty((M1, H8, mq.ROW), dtype=torch.bfloat16, device="cuda")})
+    wc = [[dev_bf16(torch, d["w_host"]) for d in lay] for _ in range(C)]
+    mq.mlaq_prewarm(H8, [M1], mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+    torch.cuda.synchronize()
+
+    def fused_graph(c):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                for d, w in zip(lay, wc[c]):
+                    mq.mlaq_run_ex(d["q_hm"].transpose(0, 1), d["pe"], w, None, None, d["out"],
+                                   mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+        return g
+
+    def staged_graph(c):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for d, w in zip(lay, wc[c]):
+                    t = torch.bmm(d["q_hm"], w)                  # [H,M,512]
+                    d["out"][..., :512].copy_(t.transpose(0, 1))  # concat, part 1
+                    d["out"][..., 512:].copy_(d["pe"])            # concat, part 2
+        return g
+
+    fg = [fused_graph(c) for c in range(C)]
+    sg = [staged_graph(c) for c in range(C)]
+    torch.cuda.synchronize()
+    f_us = time_graphs(torch, fg, args.steps, args.warmup, per_step_units=L) * 1e3
+    s_us = time_graphs(torch, sg, args.steps, args.warmup, per_step_units=L) * 1e3
+    log(f"[bench] pages' shape (K=192, H=8, M=1, BF16, 78 layers, cold): fused {f_us:.3f} us/layer, "
+        f"staged {s_us:.3f} us/layer")
+    del fg, sg, wc
+    torch.cuda.synchronize()
+
+    ab = {}
+    for H in (8, 11, 16):
+        inp = wl.make_inputs(wl.SEED["c0"] * 100 + 99, H=H, weight_format=mq.MLAQ_WEIGHT_BF16, M_draw=32, K=K)
+        w = dev_bf16(torch, inp.w)
+        for M in (1, 4, 32):
+            q_hm = dev_bf16(torch, np.ascontiguousarray(inp.q_nope[:M].transpose(1, 0, 2)))
+            pe = dev_bf16(torch, inp.q_pe[:M])
+            out = torch.empty((M, H, mq.ROW), dtype=torch.bfloat16, device="cuda")
+            mq.mlaq_prewarm(H, [M], mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+            torch.cuda.synchronize()
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(ga, stream=stream, capture_error_mode="global"):
+                    mq.mlaq_run_ex(q_hm.transpose(0, 1), pe, w, None, None, out, mq.MLAQ_WEIGHT_BF16,
+                                   mq.MLAQ_OUT_BF16)
+                with torch.cuda.graph(gb, stream=stream):
+                    t = torch.bmm(q_hm, w)
+                    out[..., :512].copy_(t.transpose(0, 1))
+                    out[..., 512:].copy_(pe)
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            fused, staged = [], []
+            for i in range(10):
+                ga.replay()
+                gb.replay()
+            torch.cuda.synchronize()
+            for i in range(args.ab_samples):
+                order = (ga, gb) if i % 2 == 0 else (gb, ga)  # balanced AB / BA
+                ev[0].record(st)
+                order[0].replay()
+                ev[1].record(st)
+                order[1].replay()
+                ev[2].record(st)
+                ev[2].synchronize()
+                t0, t1 = ev[0].elapsed_time(ev[1]) * 1e3, ev[1].elapsed_time(ev[2]) * 1e3
+                (fused if order[0] is ga else staged).append(t0)
+                (staged if order[0] is ga else fused).append(t1)
+            fm, sm = float(np.median(fused)), float(np.median(staged))
+            ab[f"H{H}_M{M}"] = {"fused_us": round(fm, 3), "staged_us": round(sm, 3), "ratio": round(fm / sm, 4)}
+            log(f"[bench] AB/BA K=192 H={H} M={M}: fused {fm:.3f} us, staged {sm:.3f} us, ratio {fm / sm:.3f}")
+            del ga, gb
+    return {"workload": "K=192 (GLM), H=8 (TP8), M=1, BF16 W and out, q_nope as a head-major [H,M,K] view, "
+                        "78 layers per hipGraph, 4 rotated weight copies (cold)",
+            "fused_us_per_layer": round(f_us, 4), "staged_us_per_layer": round(s_us, 4),
+            "pages_context_us_per_layer": {"fused": 2.880912, "staged": 4.047940,
+                                           "hardware": "eight SM12x-class GPUs, averaged over ranks (not this GPU)"},
+            "ab_ba_graph_replay": {"samples_per_shape": args.ab_samples, "shapes": ab}}
+
+
 def cpu_baseline_leg(wl, layers, budget_s):
     """The CPU oracle on the step's layers, cycling through them until the
     time budget is spent (the oracle as it stands, threaded over heads)."""
@@ -376,6 +482,7 @@ def main():
     log(f"[bench] device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
     step = decode_step_leg(torch, mq, wl, args)
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
+    pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
@@ -408,6 +515,7 @@ def main():
         "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3)},
         "floors": step["floors"],
         "per_call": per_call,
+        "pages_shape": pages,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

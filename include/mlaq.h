@@ -17,11 +17,12 @@
  * of the sparkinfer page). The summation order over k is unspecified, so the
  * BF16 projection is not a bitwise contract (sparkinfer page, "Contract").
  *
- * Fixed sizes: nope (K) = 128, latent (N) = 512, rope (R) = 64, so each output
- * row holds 576 elements. Supported plans: H in {8, 11, 16} local heads and
- * 1 <= M <= 32 tokens (vLLM page, "What" and "Layout and topology
- * behavior"); anything else is MLAQ_ERR_UNSUPPORTED and the caller keeps its
- * staged path (vLLM page, "Safety scope and PR 173").
+ * Sizes: latent (N) = 512 and rope (R) = 64, so each output row holds 576
+ * elements; nope (K) = 128, or 192 (the GLM shape of the sparkinfer page,
+ * section "What") through mlaq_run_ex. Supported plans: H in {8, 11, 16}
+ * local heads and 1 <= M <= 32 tokens (vLLM page, "What" and "Layout and
+ * topology behavior"); anything else is MLAQ_ERR_UNSUPPORTED and the caller
+ * keeps its staged path (vLLM page, "Safety scope and PR 173").
  *
  * All entry points are thread-safe. No C++ exception crosses the ABI. Every
  * buffer is caller-owned device memory; the library keeps no pointer after a
@@ -29,6 +30,8 @@
  */
 #ifndef MLAQ_H_
 #define MLAQ_H_
+
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -48,7 +51,8 @@ extern "C" {
 #define MLAQ_ERR_INVALID_ARG 2 /* bad pointer, alignment, scale presence, overlap or enum */
 #define MLAQ_ERR_DEVICE 3      /* a HIP call failed (device query or launch) */
 
-#define MLAQ_NOPE_DIM 128
+#define MLAQ_NOPE_DIM 128     /* K of mlaq_run */
+#define MLAQ_NOPE_DIM_GLM 192 /* the other K mlaq_run_ex accepts */
 #define MLAQ_LATENT_DIM 512
 #define MLAQ_ROPE_DIM 64
 #define MLAQ_MAX_M 32
@@ -62,7 +66,7 @@ extern "C" {
  * the BF16 plan does not inherit MXFP8-only requirements (same thread).
  * Returns MLAQ_OK when the fused path covers the plan, MLAQ_ERR_UNSUPPORTED
  * when it does not (arch not gfx950, H not in {8,11,16}, max_m outside
- * 1..32, dims other than 128/512/64), MLAQ_ERR_INVALID_ARG for an unknown
+ * 1..32, nope_dim not 128 or 192, latent/rope not 512/64), MLAQ_ERR_INVALID_ARG for an unknown
  * enum or a NULL arch. mlaq_last_error() says which.
  */
 int mlaq_plan_supported(int num_heads, int max_m, int nope_dim, int latent_dim, int rope_dim,
@@ -78,7 +82,8 @@ int mlaq_can_implement(int num_heads, int max_m, int nope_dim, int latent_dim, i
 
 /*
  * mlaq_prewarm -- load the kernels that serve the given token counts
- * (`m_regimes[0..n_regimes)`, each in 1..32) for H heads on `device`, and
+ * (`m_regimes[0..n_regimes)`, each in 1..32, for both nope widths) for H
+ * heads on `device`, and
  * cache the device's architecture, so later mlaq_run calls do no first-use
  * work and can be captured into a hipGraph. Deduplicates regimes that share a
  * kernel, allocates nothing that outlives the call, may block. Idempotent.
@@ -119,6 +124,42 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
 int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_scales,
              const float* q_scale, void* out, int M, int H, int weight_format, int out_dtype,
              void* stream);
+
+/*
+ * Strided / wider form of mlaq_run (same operation). Every tensor's innermost
+ * dimension is contiguous; the two outer strides are given in elements, so a
+ * head-major q_nope view ([H,M,K] storage, the batch view of the sparkinfer
+ * page's "What") and an output inside a wider, pitched workspace (vLLM page,
+ * "Layout and topology behavior": direct writes into the attention backend's
+ * query workspace; "pitched outputs" in the sparkinfer page's "Validation")
+ * need no copy.
+ *
+ *   q_nope[m,h,k]  at q_nope + m*q_stride_m + h*q_stride_h + k      (bf16)
+ *   q_pe[m,h,r]    at q_pe + m*pe_stride_m + h*pe_stride_h + r       (bf16)
+ *   out[m,h,c]     at out + m*out_stride_m + h*out_stride_h + c, c < 576
+ *   w, w_scales    contiguous [H, nope_dim, 512] and [H, nope_dim, 16]
+ *
+ * Requirements (else MLAQ_ERR_INVALID_ARG): strides >= 0 and multiples of 8
+ * elements; base pointers 16-byte aligned (q_scale 4-byte); the M*H output
+ * rows pairwise disjoint (one outer stride >= 576 and the other >= the first
+ * times its extent); the output's address span disjoint from every input's.
+ * nope_dim must be 128 or 192 (else MLAQ_ERR_UNSUPPORTED). Everything else is
+ * as for mlaq_run.
+ */
+typedef struct mlaq_run_args {
+  const void* q_nope;
+  int64_t q_stride_m, q_stride_h;
+  const void* q_pe;
+  int64_t pe_stride_m, pe_stride_h;
+  const void* w;
+  const void* w_scales;
+  const float* q_scale;
+  void* out;
+  int64_t out_stride_m, out_stride_h;
+  int M, H, nope_dim, weight_format, out_dtype;
+} mlaq_run_args;
+
+int mlaq_run_ex(const mlaq_run_args* args, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the thread's next mlaq_* call. */

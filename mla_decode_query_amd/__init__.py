@@ -15,7 +15,9 @@ The entry points carry the C names (see ``include/mlaq.h``):
   before capture (vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query
   assembly", "Layout and topology behavior");
 * ``mlaq_run``            -- one fused call: ``[M,H,576]`` output with q_pe
-  appended in the same launch (sparkinfer page, "What"; vLLM page, "What").
+  appended in the same launch (sparkinfer page, "What"; vLLM page, "What");
+* ``mlaq_run_ex``         -- the same with strided views (a head-major q_nope,
+  a pitched output workspace) and nope width 128 or 192.
 """
 
 from __future__ import annotations
@@ -32,10 +34,22 @@ MLAQ_WEIGHT_BF16, MLAQ_WEIGHT_MXFP8 = 0, 1
 MLAQ_OUT_BF16, MLAQ_OUT_E4M3 = 0, 1
 MLAQ_OK, MLAQ_ERR_UNSUPPORTED, MLAQ_ERR_INVALID_ARG, MLAQ_ERR_DEVICE = 0, 1, 2, 3
 NOPE_DIM, LATENT_DIM, ROPE_DIM, MAX_M = 128, 512, 64, 32
+NOPE_DIM_GLM = 192
 ROW = LATENT_DIM + ROPE_DIM
 MX_BLOCK = 32
 
 _STATUS_NAMES = {0: "MLAQ_OK", 1: "MLAQ_ERR_UNSUPPORTED", 2: "MLAQ_ERR_INVALID_ARG", 3: "MLAQ_ERR_DEVICE"}
+
+
+class RunArgs(ctypes.Structure):
+    """Mirror of ``mlaq_run_args`` in include/mlaq.h (same field order and types)."""
+
+    _fields_ = [("q_nope", ctypes.c_void_p), ("q_stride_m", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("q_pe", ctypes.c_void_p), ("pe_stride_m", ctypes.c_int64), ("pe_stride_h", ctypes.c_int64),
+                ("w", ctypes.c_void_p), ("w_scales", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("out_stride_m", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
+                ("M", ctypes.c_int), ("H", ctypes.c_int), ("nope_dim", ctypes.c_int),
+                ("weight_format", ctypes.c_int), ("out_dtype", ctypes.c_int)]
 
 
 class MlaqError(RuntimeError):
@@ -65,6 +79,8 @@ def library() -> ctypes.CDLL:
         lib.mlaq_prewarm.restype = I
         lib.mlaq_run.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
         lib.mlaq_run.restype = I
+        lib.mlaq_run_ex.argtypes = [ctypes.POINTER(RunArgs), P]
+        lib.mlaq_run_ex.restype = I
         lib.mlaq_last_error.argtypes = []
         lib.mlaq_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -159,6 +175,52 @@ def mlaq_run(q_nope: torch.Tensor, q_pe: torch.Tensor, w: torch.Tensor, w_scales
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _check(library().mlaq_run(_ptr(q_nope), _ptr(q_pe), _ptr(w), _ptr(w_scales), _ptr(q_scale), _ptr(out),
                               M, H, weight_format, out_dtype, ctypes.c_void_p(s.cuda_stream)))
+
+
+def _expect_view(t, name, dtype, shape, device):
+    """A [M,H,width] view whose innermost dimension is contiguous."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be a 3-d view with a contiguous last dimension")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.stride(0), t.stride(1)
+
+
+def mlaq_run_ex(q_nope: torch.Tensor, q_pe: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None,
+                q_scale: torch.Tensor | None, out: torch.Tensor, weight_format: int, out_dtype: int,
+                stream: torch.cuda.Stream | None = None) -> None:
+    """Like ``mlaq_run`` but ``q_nope`` ([M,H,K], K = 128 or 192), ``q_pe`` and
+    ``out`` may be strided views (e.g. ``q.transpose(0, 1)`` of a head-major
+    [H,M,K] tensor, or ``ws[..., :576]`` of a wider workspace). Weights stay
+    contiguous [H,K,512] (and [H,K,16] scales)."""
+    if q_nope.dim() != 3:
+        raise ValueError("q_nope must be [M,H,K]")
+    M, H, K = (int(x) for x in q_nope.shape)
+    dev = q_nope.device
+    q_sm, q_sh = _expect_view(q_nope, "q_nope", torch.bfloat16, (M, H, K), dev)
+    pe_sm, pe_sh = _expect_view(q_pe, "q_pe", torch.bfloat16, (M, H, ROPE_DIM), dev)
+    wdt = torch.bfloat16 if weight_format == MLAQ_WEIGHT_BF16 else (
+        w.dtype if w.dtype in (torch.float8_e4m3fn, torch.uint8) else torch.float8_e4m3fn)
+    _expect(w, "w", wdt, (H, K, LATENT_DIM), dev)
+    if w_scales is not None:
+        _expect(w_scales, "w_scales",
+                w_scales.dtype if w_scales.dtype in (torch.uint8, torch.float8_e8m0fnu) else torch.uint8,
+                (H, K, LATENT_DIM // MX_BLOCK), dev)
+    if q_scale is not None:
+        _expect(q_scale, "q_scale", torch.float32, (1,), dev)
+    odt = torch.bfloat16 if out_dtype == MLAQ_OUT_BF16 else (
+        out.dtype if out.dtype in (torch.float8_e4m3fn, torch.uint8) else torch.float8_e4m3fn)
+    o_sm, o_sh = _expect_view(out, "out", odt, (M, H, ROW), dev)
+    args = RunArgs(q_nope.data_ptr(), q_sm, q_sh, q_pe.data_ptr(), pe_sm, pe_sh, w.data_ptr(),
+                   None if w_scales is None else w_scales.data_ptr(),
+                   None if q_scale is None else q_scale.data_ptr(), out.data_ptr(), o_sm, o_sh,
+                   M, H, K, weight_format, out_dtype)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(library().mlaq_run_ex(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
 
 
 def fused_query(q_nope, q_pe, w, w_scales=None, q_scale=None, out_dtype: int = MLAQ_OUT_BF16, out=None):

@@ -39,8 +39,9 @@ int common_plan(int num_heads, int max_m, int nope_dim, int latent_dim, int rope
   if (!supported_heads(num_heads))
     return fail(MLAQ_ERR_UNSUPPORTED, "num_heads=%d not in {8, 11, 16}", num_heads);
   if (max_m < 1 || max_m > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "max_m=%d outside 1..32", max_m);
-  if (nope_dim != MLAQ_NOPE_DIM || latent_dim != MLAQ_LATENT_DIM || rope_dim != MLAQ_ROPE_DIM)
-    return fail(MLAQ_ERR_UNSUPPORTED, "dims (nope %d, latent %d, rope %d) are not (128, 512, 64)", nope_dim,
+  if ((nope_dim != MLAQ_NOPE_DIM && nope_dim != MLAQ_NOPE_DIM_GLM) || latent_dim != MLAQ_LATENT_DIM ||
+      rope_dim != MLAQ_ROPE_DIM)
+    return fail(MLAQ_ERR_UNSUPPORTED, "dims (nope %d, latent %d, rope %d) are not (128 or 192, 512, 64)", nope_dim,
                 latent_dim, rope_dim);
   return MLAQ_OK;
 }
@@ -99,6 +100,23 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Bytes spanned by an [M,H,width] view with outer strides (sm, sh) elements.
+size_t span_bytes(int M, int H, int64_t sm, int64_t sh, int width, size_t esz) {
+  return size_t((int64_t(M) - 1) * sm + (int64_t(H) - 1) * sh + width) * esz;
+}
+
+constexpr int64_t kMaxStride = int64_t(1) << 36; // keeps every span far from overflow
+
+bool stride_ok(int64_t s) { return s >= 0 && s < kMaxStride && s % 8 == 0; }
+
+// The M*H output rows [off, off + 576) are pairwise disjoint when one outer
+// stride clears a row and the other clears all rows along the first.
+bool rows_disjoint(int M, int H, int64_t sm, int64_t sh) {
+  const int64_t row = mlaq::kRow;
+  if (M == 1) return sh >= row;
+  return (sh >= row && sm >= int64_t(H) * sh) || (sm >= row && sh >= int64_t(M) * sm);
+}
+
 } // namespace
 
 extern "C" {
@@ -129,48 +147,61 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
     st = plan_for(num_heads, m_regimes[i], MLAQ_NOPE_DIM, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, weight_format, out_dtype,
                   arch);
     if (st != MLAQ_OK) return st;
-    const mlaq::Variant v = mlaq::variant_for(weight_format, out_dtype, m_regimes[i]);
-    if (seen[v.m_tiles]) continue;
-    seen[v.m_tiles] = true;
+    const int tiles = mlaq::variant_for(weight_format, out_dtype, m_regimes[i], mlaq::kNope).m_tiles;
+    if (seen[tiles]) continue;
+    seen[tiles] = true;
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != device) e = hipSetDevice(device);
-    hipFuncAttributes attr;
-    if (e == hipSuccess) e = hipFuncGetAttributes(&attr, mlaq::kernel_for(v));
+    for (int K : {mlaq::kNope, mlaq::kNopeGlm}) {
+      hipFuncAttributes attr;
+      if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, mlaq::kernel_for(mlaq::variant_for(weight_format, out_dtype, m_regimes[i], K)));
+    }
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
   }
   return MLAQ_OK;
 }
 
-int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_scales, const float* q_scale,
-             void* out, int M, int H, int weight_format, int out_dtype, void* stream) {
+int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   clear_error();
-  if (!known_weight_format(weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", weight_format);
-  if (!known_out_dtype(out_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!args) return fail(MLAQ_ERR_INVALID_ARG, "args is NULL");
+  const mlaq_run_args& a = *args;
+  const int M = a.M, H = a.H, K = a.nope_dim;
+  if (!known_weight_format(a.weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", a.weight_format);
+  if (!known_out_dtype(a.out_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown out_dtype %d", a.out_dtype);
   if (!supported_heads(H)) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d not in {8, 11, 16}", H);
   if (M < 0 || M > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "M=%d outside 0..32", M);
+  if (K != MLAQ_NOPE_DIM && K != MLAQ_NOPE_DIM_GLM) return fail(MLAQ_ERR_UNSUPPORTED, "nope_dim=%d not 128 or 192", K);
   if (M == 0) return MLAQ_OK; // empty batch: nothing to read or write
-  if (!q_nope || !q_pe || !w || !out) return fail(MLAQ_ERR_INVALID_ARG, "q_nope, q_pe, w and out must be non-NULL");
-  if (weight_format == MLAQ_WEIGHT_MXFP8 && !w_scales)
+  if (!a.q_nope || !a.q_pe || !a.w || !a.out)
+    return fail(MLAQ_ERR_INVALID_ARG, "q_nope, q_pe, w and out must be non-NULL");
+  if (a.weight_format == MLAQ_WEIGHT_MXFP8 && !a.w_scales)
     return fail(MLAQ_ERR_INVALID_ARG, "MXFP8 weights need w_scales");
-  if (weight_format == MLAQ_WEIGHT_BF16 && w_scales)
+  if (a.weight_format == MLAQ_WEIGHT_BF16 && a.w_scales)
     return fail(MLAQ_ERR_INVALID_ARG, "BF16 weights take no w_scales (pass NULL)");
-  if (out_dtype == MLAQ_OUT_E4M3 && !q_scale) return fail(MLAQ_ERR_INVALID_ARG, "E4M3 output needs q_scale");
-  if (out_dtype == MLAQ_OUT_BF16 && q_scale)
+  if (a.out_dtype == MLAQ_OUT_E4M3 && !a.q_scale) return fail(MLAQ_ERR_INVALID_ARG, "E4M3 output needs q_scale");
+  if (a.out_dtype == MLAQ_OUT_BF16 && a.q_scale)
     return fail(MLAQ_ERR_INVALID_ARG, "BF16 output takes no q_scale (pass NULL)");
-  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w, 16) || !aligned(out, 16))
+  if (!aligned(a.q_nope, 16) || !aligned(a.q_pe, 16) || !aligned(a.w, 16) || !aligned(a.out, 16))
     return fail(MLAQ_ERR_INVALID_ARG, "q_nope, q_pe, w and out must be 16-byte aligned");
-  if (q_scale && !aligned(q_scale, 4)) return fail(MLAQ_ERR_INVALID_ARG, "q_scale must be 4-byte aligned");
+  if (a.q_scale && !aligned(a.q_scale, 4)) return fail(MLAQ_ERR_INVALID_ARG, "q_scale must be 4-byte aligned");
+  if (!stride_ok(a.q_stride_m) || !stride_ok(a.q_stride_h) || !stride_ok(a.pe_stride_m) ||
+      !stride_ok(a.pe_stride_h) || !stride_ok(a.out_stride_m) || !stride_ok(a.out_stride_h))
+    return fail(MLAQ_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements below 2^36");
+  if (!rows_disjoint(M, H, a.out_stride_m, a.out_stride_h))
+    return fail(MLAQ_ERR_INVALID_ARG, "out strides (%lld, %lld) make output rows overlap",
+                (long long)a.out_stride_m, (long long)a.out_stride_h);
 
-  const size_t mh = size_t(M) * size_t(H);
-  const size_t esz_w = weight_format == MLAQ_WEIGHT_BF16 ? 2 : 1;
-  const size_t esz_o = out_dtype == MLAQ_OUT_BF16 ? 2 : 1;
-  const size_t out_bytes = mh * mlaq::kRow * esz_o;
-  if (overlaps(out, out_bytes, q_nope, mh * mlaq::kNope * 2) || overlaps(out, out_bytes, q_pe, mh * mlaq::kRope * 2) ||
-      overlaps(out, out_bytes, w, size_t(H) * mlaq::kNope * mlaq::kLatent * esz_w) ||
-      overlaps(out, out_bytes, w_scales, size_t(H) * mlaq::kNope * (mlaq::kLatent / mlaq::kMxBlock)) ||
-      overlaps(out, out_bytes, q_scale, sizeof(float)))
+  const size_t esz_w = a.weight_format == MLAQ_WEIGHT_BF16 ? 2 : 1;
+  const size_t esz_o = a.out_dtype == MLAQ_OUT_BF16 ? 2 : 1;
+  const size_t out_bytes = span_bytes(M, H, a.out_stride_m, a.out_stride_h, mlaq::kRow, esz_o);
+  if (overlaps(a.out, out_bytes, a.q_nope, span_bytes(M, H, a.q_stride_m, a.q_stride_h, K, 2)) ||
+      overlaps(a.out, out_bytes, a.q_pe, span_bytes(M, H, a.pe_stride_m, a.pe_stride_h, mlaq::kRope, 2)) ||
+      overlaps(a.out, out_bytes, a.w, size_t(H) * K * mlaq::kLatent * esz_w) ||
+      overlaps(a.out, out_bytes, a.w_scales, size_t(H) * K * (mlaq::kLatent / mlaq::kMxBlock)) ||
+      overlaps(a.out, out_bytes, a.q_scale, sizeof(float)))
     return fail(MLAQ_ERR_INVALID_ARG, "out overlaps an input buffer");
 
   int device = 0;
@@ -179,20 +210,45 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
   const char* arch = nullptr;
   int st = device_arch(device, &arch);
   if (st != MLAQ_OK) return st;
-  st = plan_for(H, M, MLAQ_NOPE_DIM, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, weight_format, out_dtype, arch);
+  st = plan_for(H, M, K, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, a.weight_format, a.out_dtype, arch);
   if (st != MLAQ_OK) return st;
 
-  const mlaq::Variant v = mlaq::variant_for(weight_format, out_dtype, M);
+  const mlaq::Variant v = mlaq::variant_for(a.weight_format, a.out_dtype, M, K);
   const void* fn = mlaq::kernel_for(v);
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
   mlaq::launch_shape(v, H, &grid, &block);
-  mlaq::FusedArgs args{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe), w,
-                       static_cast<const uint8_t*>(w_scales), q_scale, out, M, H};
-  void* kargs[] = {&args};
+  mlaq::FusedArgs ka{static_cast<const uint16_t*>(a.q_nope), static_cast<const uint16_t*>(a.q_pe), a.w,
+                     static_cast<const uint8_t*>(a.w_scales), a.q_scale, a.out,
+                     a.q_stride_m, a.q_stride_h, a.pe_stride_m, a.pe_stride_h, a.out_stride_m, a.out_stride_h,
+                     M, H};
+  void* kargs[] = {&ka};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;
+}
+
+int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_scales, const float* q_scale,
+             void* out, int M, int H, int weight_format, int out_dtype, void* stream) {
+  mlaq_run_args a;
+  a.q_nope = q_nope;
+  a.q_stride_m = int64_t(H) * mlaq::kNope;
+  a.q_stride_h = mlaq::kNope;
+  a.q_pe = q_pe;
+  a.pe_stride_m = int64_t(H) * mlaq::kRope;
+  a.pe_stride_h = mlaq::kRope;
+  a.w = w;
+  a.w_scales = w_scales;
+  a.q_scale = q_scale;
+  a.out = out;
+  a.out_stride_m = int64_t(H) * mlaq::kRow;
+  a.out_stride_h = mlaq::kRow;
+  a.M = M;
+  a.H = H;
+  a.nope_dim = mlaq::kNope;
+  a.weight_format = weight_format;
+  a.out_dtype = out_dtype;
+  return mlaq_run_ex(&a, stream);
 }
 
 const char* mlaq_last_error(void) { return g_err; }

@@ -7,21 +7,24 @@
 
 namespace mlaq {
 
-constexpr int kNope = 128;   // K: reduction width
+constexpr int kNope = 128;   // K of the contiguous entry point (mlaq_run)
+constexpr int kNopeGlm = 192; // the other supported K (the GLM shape)
 constexpr int kLatent = 512; // N: projection width
 constexpr int kRope = 64;    // R: appended q_pe width
 constexpr int kRow = kLatent + kRope;
 constexpr int kMxBlock = 32; // E8M0 scale group along n
 constexpr int kMaxM = 32;
 
-// Kernel arguments, passed by value (one kernarg segment).
+// Kernel arguments, passed by value (one kernarg segment). Strides are in
+// elements; the innermost dimension of every tensor is contiguous.
 struct FusedArgs {
-  const uint16_t* q_nope; // bf16 [M,H,K]
-  const uint16_t* q_pe;   // bf16 [M,H,R]
-  const void* w;          // bf16 or E4M3 [H,K,N]
-  const uint8_t* w_scales; // E8M0 [H,K,N/32] or null
-  const float* q_scale;   // device fp32 or null
-  void* out;              // bf16 or E4M3 [M,H,N+R]
+  const uint16_t* q_nope;  // bf16 [M,H,K] at (q_sm, q_sh, 1)
+  const uint16_t* q_pe;    // bf16 [M,H,R] at (pe_sm, pe_sh, 1)
+  const void* w;           // bf16 or E4M3 [H,K,N], contiguous
+  const uint8_t* w_scales; // E8M0 [H,K,N/32], contiguous, or null
+  const float* q_scale;    // device fp32 or null
+  void* out;               // bf16 or E4M3 [M,H,N+R] at (out_sm, out_sh, 1)
+  int64_t q_sm, q_sh, pe_sm, pe_sh, out_sm, out_sh;
   int M;
   int H;
 };
@@ -31,10 +34,11 @@ struct Variant {
   int weight_format; // MLAQ_WEIGHT_*
   int out_dtype;     // MLAQ_OUT_*
   int m_tiles;       // 16-token tiles: 1 (M <= 16) or 2 (M <= 32)
+  int nope;          // K: 128 or 192
 };
 
-inline Variant variant_for(int weight_format, int out_dtype, int M) {
-  return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2};
+inline Variant variant_for(int weight_format, int out_dtype, int M, int nope) {
+  return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2, nope};
 }
 
 // Host function pointer of the kernel for a variant (null if none).

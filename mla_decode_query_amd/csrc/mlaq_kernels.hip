@@ -8,11 +8,12 @@
 //   out[m,h,512:576] = cvt(q_pe[m,h,:])
 // with cvt = identity (BF16 output) or e4m3_satfinite(x / q_scale).
 //
-// Decomposition. The call moves ~1-2 MiB of weights and little else, so the
+// Decomposition. The call moves ~1-3 MiB of weights and little else, so the
 // kernel is an HBM stream whose cost is latency: every weight byte is
 // requested at kernel entry, spread over as many CUs as the tiling allows.
-// A workgroup (4 waves) owns one head h and one slice of WCOLS = 16*VEC
-// latent columns, over all 128 k. Wave w takes k rows [32w, 32w+32).
+// A workgroup of K/32 waves (4 for K = 128, 6 for K = 192) owns one head h
+// and one slice of WCOLS = 16*VEC latent columns, over all K. Wave w takes k
+// rows [32w, 32w+32).
 //
 // Contraction on MFMA without any transpose. v_mfma_f32_16x16x32_bf16 pairs
 // element e of lane (i + 16g) of A with element e of lane (j + 16g) of B, for
@@ -26,8 +27,8 @@
 // 4 lane groups walk the 4 k octets, and no LDS round trip is needed for
 // either operand. M <= 16 uses one 16-token tile, M <= 32 two.
 //
-// The four waves' fp32 partial tiles are summed through LDS in a fixed order
-// (wave 0 + 1 + 2 + 3), so results are deterministic. The epilogue rounds to
+// The waves' fp32 partial tiles are summed through LDS in a fixed order
+// (wave 0 + 1 + 2 + ...), so results are deterministic. The epilogue rounds to
 // bf16 (and for E4M3 output divides by q_scale and encodes), and the same
 // workgroups copy q_pe into columns 512..575 of the row, storing it before
 // they wait for their weights.
@@ -48,7 +49,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256; // 4 waves of 64
 constexpr int kScalesPerRow = kLatent / kMxBlock;
 
 // ---------------------------------------------------------------------------
@@ -143,8 +143,10 @@ __device__ __forceinline__ int tile_of_block(int b, int nblocks) {
 // The fused kernel
 // ---------------------------------------------------------------------------
 
-template <int WF, int OF, int MT, int VEC>
-__global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
+template <int WF, int OF, int MT, int VEC, int NW>
+__global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
+  constexpr int K = 32 * NW;                            // reduction width
+  constexpr int THREADS = 64 * NW;
   constexpr int ESZ = (WF == MLAQ_WEIGHT_BF16) ? 2 : 1; // bytes per weight
   constexpr int WCOLS = 16 * VEC;                       // latent columns per workgroup
   constexpr int NCT = kLatent / WCOLS;                  // column tiles per head
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
   static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
   static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 2 == 0, "E4M3 columns are decoded in pairs");
-  __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
+  __shared__ __attribute__((aligned(16))) float part[NW * MROWS * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   const int tile = tile_of_block(blockIdx.x, gridDim.x);
   const int h = tile / NCT, ct = tile - h * NCT;
   const int c0 = ct * WCOLS;
-  const int H = a.H, M = a.M;
+  const int M = a.M;
   const int k0 = 32 * wave + 8 * g; // first of this lane's 8 k rows
   const int col = c0 + VEC * j;     // first of this lane's VEC columns
 
@@ -173,20 +175,20 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   const bool has_pe = pe_chunk < M * (kRope / 8);
   const int pe_x = has_pe ? pe_chunk : 0; // loads stay unconditional (no branch, no early wait)
   const int pe_m = pe_x >> 3, pe_c = pe_x & 7;
-  const u32x4_t pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + (size_t(pe_m) * H + h) * kRope + 8 * pe_c);
+  const u32x4_t pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + pe_m * a.pe_sm + h * a.pe_sh + 8 * pe_c);
   __builtin_amdgcn_sched_barrier(0); // keep the q_pe load ahead of the weight loads
 
   // 2. Weight rows (the bulk of the bytes), all requested up front.
   uint32_t wr[8][D];
   {
     const uint8_t* base =
-        static_cast<const uint8_t*>(a.w) + ((size_t(h) * kNope + k0) * kLatent + col) * ESZ;
+        static_cast<const uint8_t*>(a.w) + ((size_t(h) * K + k0) * kLatent + col) * ESZ;
 #pragma unroll
     for (int r = 0; r < 8; ++r) load_row<RB>(base + size_t(r) * kLatent * ESZ, wr[r]);
   }
   uint32_t sc[8];
   if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
-    const uint8_t* sb = a.w_scales + (size_t(h) * kNope + k0) * kScalesPerRow + col / kMxBlock;
+    const uint8_t* sb = a.w_scales + (size_t(h) * K + k0) * kScalesPerRow + col / kMxBlock;
 #pragma unroll
     for (int r = 0; r < 8; ++r) sc[r] = sb[r * kScalesPerRow];
   }
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + j;
     const int mc = m < M ? m : 0;
-    qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + (size_t(mc) * H + h) * kNope + k0);
+    qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + mc * a.q_sm + h * a.q_sh + k0);
   }
   __builtin_amdgcn_sched_barrier(0); // all loads are in flight before any wait
 
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
     rqs = 1.0f / qs;
   }
   if (has_pe) {
-    const size_t o = (size_t(pe_m) * H + h) * kRow + kLatent + 8 * pe_c;
+    const int64_t o = pe_m * a.out_sm + h * a.out_sh + kLatent + 8 * pe_c;
     if constexpr (OF == MLAQ_OUT_BF16) {
       *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = pe_v;
     } else {
@@ -289,18 +291,16 @@ __global__ __launch_bounds__(kThreads) void fused_query_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // 6. Epilogue: sum the four k slices in a fixed order, round, convert and
+  // 6. Epilogue: sum the k slices in a fixed order, round, convert and
   //    store; each thread finishes 4 consecutive columns of one token.
   constexpr int GPR = WCOLS / 4;
-  for (int x = tid; x < M * GPR; x += kThreads) {
+  for (int x = tid; x < M * GPR; x += THREADS) {
     const int m = x / GPR, cg = x - m * GPR;
     const int off = m * LDW + 4 * cg;
-    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(part + off);
-    const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(part + MROWS * LDW + off);
-    const f32x4_t p2 = *reinterpret_cast<const f32x4_t*>(part + 2 * MROWS * LDW + off);
-    const f32x4_t p3 = *reinterpret_cast<const f32x4_t*>(part + 3 * MROWS * LDW + off);
-    const f32x4_t sum = ((p0 + p1) + p2) + p3;
-    const size_t o = (size_t(m) * H + h) * kRow + c0 + 4 * cg;
+    f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
+    const int64_t o = m * a.out_sm + h * a.out_sh + c0 + 4 * cg;
     const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
     const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
     if constexpr (OF == MLAQ_OUT_BF16) {
@@ -324,25 +324,29 @@ constexpr int vec_of() {
   return WF == MLAQ_WEIGHT_BF16 ? 2 : (MT == 1 ? 4 : 2);
 }
 
-template <int WF, int OF, int MT>
+template <int WF, int OF, int MT, int NW>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>()>);
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>(), NW>);
 }
 
 } // namespace
 
 const void* kernel_for(const Variant& v) {
-#define MLAQ_CASE(WF, OF, MT)                                              \
-  if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT) \
-    return kernel_ptr<WF, OF, MT>();
-  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1)
-  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 2)
-  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 1)
-  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 2)
-  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 1)
-  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 2)
-  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 1)
-  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 2)
+#define MLAQ_CASE(WF, OF, MT, K)                                                            \
+  if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT && v.nope == K) \
+    return kernel_ptr<WF, OF, MT, K / 32>();
+#define MLAQ_CASES(K)                                \
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1, K)  \
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 2, K)  \
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 1, K)  \
+  MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_E4M3, 2, K)  \
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 1, K) \
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_BF16, 2, K) \
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 1, K) \
+  MLAQ_CASE(MLAQ_WEIGHT_MXFP8, MLAQ_OUT_E4M3, 2, K)
+  MLAQ_CASES(128)
+  MLAQ_CASES(192)
+#undef MLAQ_CASES
 #undef MLAQ_CASE
   return nullptr;
 }
@@ -352,7 +356,7 @@ void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
   if (v.weight_format == MLAQ_WEIGHT_MXFP8)
     vec = v.m_tiles == 1 ? vec_of<MLAQ_WEIGHT_MXFP8, 1>() : vec_of<MLAQ_WEIGHT_MXFP8, 2>();
   *grid = dim3(unsigned(H * (kLatent / (16 * vec))), 1, 1);
-  *block = dim3(kThreads, 1, 1);
+  *block = dim3(unsigned(64 * (v.nope / 32)), 1, 1);
 }
 
 } // namespace mlaq

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"mlaq_plan_supported", "mlaq_can_implement", "mlaq_prewarm",
-                                         "mlaq_run", "mlaq_last_error"}
+                                         "mlaq_run", "mlaq_run_ex", "mlaq_last_error"}
 
 
 def test_library_exports_every_declared_function(lib):
@@ -41,8 +41,8 @@ def test_library_exports_every_declared_function(lib):
 def test_python_constants_match_header():
     defines = dict(re.findall(r"#define\s+(MLAQ_\w+)\s+(\d+)", HEADER.read_text()))
     for name, value in defines.items():
-        key = {"MLAQ_NOPE_DIM": "NOPE_DIM", "MLAQ_LATENT_DIM": "LATENT_DIM", "MLAQ_ROPE_DIM": "ROPE_DIM",
-               "MLAQ_MAX_M": "MAX_M"}.get(name, name)
+        key = {"MLAQ_NOPE_DIM": "NOPE_DIM", "MLAQ_NOPE_DIM_GLM": "NOPE_DIM_GLM", "MLAQ_LATENT_DIM": "LATENT_DIM",
+               "MLAQ_ROPE_DIM": "ROPE_DIM", "MLAQ_MAX_M": "MAX_M"}.get(name, name)
         assert getattr(mq, key) == int(value), name
 
 
@@ -53,9 +53,10 @@ OK, UNS, INV = mq.MLAQ_OK, mq.MLAQ_ERR_UNSUPPORTED, mq.MLAQ_ERR_INVALID_ARG
 @pytest.mark.parametrize("od", [0, 1])
 @pytest.mark.parametrize("h", [8, 11, 16])
 @pytest.mark.parametrize("m", [1, 17, 32])
-def test_gate_accepts_supported_plans(lib, wf, od, h, m):
-    assert mq.mlaq_plan_supported(h, m, weight_format=wf, out_dtype=od, arch="gfx950:sramecc+:xnack-") == OK
-    assert mq.mlaq_plan_supported(h, m, weight_format=wf, out_dtype=od, arch="gfx950") == OK
+@pytest.mark.parametrize("k", [128, 192])
+def test_gate_accepts_supported_plans(lib, wf, od, h, m, k):
+    assert mq.mlaq_plan_supported(h, m, k, weight_format=wf, out_dtype=od, arch="gfx950:sramecc+:xnack-") == OK
+    assert mq.mlaq_plan_supported(h, m, k, weight_format=wf, out_dtype=od, arch="gfx950") == OK
 
 
 @pytest.mark.parametrize("args,status,msg", [
@@ -63,7 +64,8 @@ def test_gate_accepts_supported_plans(lib, wf, od, h, m):
     (dict(num_heads=4, max_m=1), UNS, "num_heads"),
     (dict(num_heads=16, max_m=0), UNS, "max_m"),
     (dict(num_heads=16, max_m=33), UNS, "max_m"),
-    (dict(num_heads=16, max_m=4, nope_dim=192), UNS, "dims"),
+    (dict(num_heads=16, max_m=4, nope_dim=256), UNS, "dims"),
+    (dict(num_heads=16, max_m=4, nope_dim=64), UNS, "dims"),
     (dict(num_heads=16, max_m=4, latent_dim=256), UNS, "dims"),
     (dict(num_heads=16, max_m=4, rope_dim=32), UNS, "dims"),
     (dict(num_heads=16, max_m=4, arch="gfx942:sramecc+:xnack-"), UNS, "not gfx950"),
@@ -136,3 +138,69 @@ def test_prewarm_rejects_bad_regimes_before_device(lib):
     assert lib.mlaq_prewarm(16, None, 3, 0, 0, 0) == INV
     assert lib.mlaq_prewarm(16, None, -1, 0, 0, 0) == INV
     assert lib.mlaq_prewarm(16, None, 0, 0, 0, 99) == INV  # device ordinal out of range
+
+
+HEADER_PROBE = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "mlaq.h"
+int main(void) {
+  printf("%zu", sizeof(mlaq_run_args));
+#define F(x) printf(" %zu", offsetof(mlaq_run_args, x));
+  F(q_nope) F(q_stride_m) F(q_stride_h) F(q_pe) F(pe_stride_m) F(pe_stride_h) F(w) F(w_scales) F(q_scale)
+  F(out) F(out_stride_m) F(out_stride_h) F(M) F(H) F(nope_dim) F(weight_format) F(out_dtype)
+  printf("\n");
+  return 0;
+}
+"""
+
+
+def test_run_args_layout_matches_header(tmp_path):
+    """The binding's ctypes mirror has the C struct's size and field offsets
+    (the header compiled by gcc as a C program)."""
+    import subprocess
+
+    src = tmp_path / "probe.c"
+    src.write_text(HEADER_PROBE)
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", f"-I{HEADER.parent}", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(mq.RunArgs)] + [getattr(mq.RunArgs, name).offset for name, _ in mq.RunArgs._fields_]
+    assert got == want
+
+
+def run_ex(lib, **kw):
+    a = mq.RunArgs(A, 2048, 128, 2 * A, 1024, 64, 4 * A, None, None, 8 * A, 16 * 576, 576, 4, 16, 128, 0, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.mlaq_run_ex(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(nope_dim=256), UNS, "nope_dim=256"),
+    (dict(nope_dim=64), UNS, "nope_dim=64"),
+    (dict(q_stride_m=-8), INV, "strides"),
+    (dict(q_stride_h=100), INV, "strides"),
+    (dict(pe_stride_h=4), INV, "strides"),
+    (dict(out_stride_h=572), INV, "strides"),
+    (dict(out_stride_h=1 << 37), INV, "strides"),
+    (dict(out_stride_h=568), INV, "overlap"),          # rows of 576 elements would overlap
+    (dict(out_stride_m=576 * 8), INV, "overlap"),      # m-major but tokens collide with heads
+    (dict(out_stride_m=0, out_stride_h=576), INV, "overlap"),
+    (dict(out=2 * A + 4096), INV, "overlaps an input"),
+    (dict(q_nope=None), INV, "non-NULL"),
+    (dict(w=4 * A + 8), INV, "16-byte aligned"),
+    (dict(weight_format=1), INV, "need w_scales"),
+    (dict(out_dtype=1), INV, "needs q_scale"),
+    (dict(H=12), UNS, "H=12"),
+    (dict(M=40), UNS, "M=40"),
+])
+def test_run_ex_rejects_before_any_device_call(lib, kw, status, msg):
+    assert run_ex(lib, **kw) == status
+    assert msg in mq.mlaq_last_error()
+
+
+def test_run_ex_null_args_and_empty_batch(lib):
+    assert lib.mlaq_run_ex(None, None) == INV
+    assert "NULL" in mq.mlaq_last_error()
+    assert run_ex(lib, M=0, q_nope=None, out=None, nope_dim=192) == OK
