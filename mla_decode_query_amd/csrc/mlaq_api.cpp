@@ -105,9 +105,7 @@ size_t span_bytes(int M, int H, int64_t sm, int64_t sh, int width, size_t esz) {
   return size_t((int64_t(M) - 1) * sm + (int64_t(H) - 1) * sh + width) * esz;
 }
 
-constexpr int64_t kMaxStride = int64_t(1) << 36; // keeps every span far from overflow
-
-bool stride_ok(int64_t s) { return s >= 0 && s < kMaxStride && s % 8 == 0; }
+bool stride_ok(int64_t s) { return s >= 0 && s < mlaq::kMaxStride && s % 8 == 0; }
 
 // The M*H output rows [off, off + 576) are pairwise disjoint when one outer
 // stride clears a row and the other clears all rows along the first.
@@ -189,7 +187,7 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   if (a.q_scale && !aligned(a.q_scale, 4)) return fail(MLAQ_ERR_INVALID_ARG, "q_scale must be 4-byte aligned");
   if (!stride_ok(a.q_stride_m) || !stride_ok(a.q_stride_h) || !stride_ok(a.pe_stride_m) ||
       !stride_ok(a.pe_stride_h) || !stride_ok(a.out_stride_m) || !stride_ok(a.out_stride_h))
-    return fail(MLAQ_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements below 2^36");
+    return fail(MLAQ_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements below 2^24");
   if (!rows_disjoint(M, H, a.out_stride_m, a.out_stride_h))
     return fail(MLAQ_ERR_INVALID_ARG, "out strides (%lld, %lld) make output rows overlap",
                 (long long)a.out_stride_m, (long long)a.out_stride_h);
@@ -220,8 +218,8 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   mlaq::launch_shape(v, H, &grid, &block);
   mlaq::FusedArgs ka{static_cast<const uint16_t*>(a.q_nope), static_cast<const uint16_t*>(a.q_pe), a.w,
                      static_cast<const uint8_t*>(a.w_scales), a.q_scale, a.out,
-                     a.q_stride_m, a.q_stride_h, a.pe_stride_m, a.pe_stride_h, a.out_stride_m, a.out_stride_h,
-                     M, H};
+                     uint32_t(a.q_stride_m), uint32_t(a.q_stride_h), uint32_t(a.pe_stride_m),
+                     uint32_t(a.pe_stride_h), uint32_t(a.out_stride_m), uint32_t(a.out_stride_h), M, H};
   void* kargs[] = {&ka};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));

@@ -14,9 +14,11 @@ constexpr int kRope = 64;    // R: appended q_pe width
 constexpr int kRow = kLatent + kRope;
 constexpr int kMxBlock = 32; // E8M0 scale group along n
 constexpr int kMaxM = 32;
+constexpr int64_t kMaxStride = int64_t(1) << 24; // elements; keeps kernel offsets 32-bit
 
 // Kernel arguments, passed by value (one kernarg segment). Strides are in
-// elements; the innermost dimension of every tensor is contiguous.
+// elements (below 2^24, so offsets stay 32-bit and multiplies 24-bit); the
+// innermost dimension of every tensor is contiguous.
 struct FusedArgs {
   const uint16_t* q_nope;  // bf16 [M,H,K] at (q_sm, q_sh, 1)
   const uint16_t* q_pe;    // bf16 [M,H,R] at (pe_sm, pe_sh, 1)
@@ -24,7 +26,7 @@ struct FusedArgs {
   const uint8_t* w_scales; // E8M0 [H,K,N/32], contiguous, or null
   const float* q_scale;    // device fp32 or null
   void* out;               // bf16 or E4M3 [M,H,N+R] at (out_sm, out_sh, 1)
-  int64_t q_sm, q_sh, pe_sm, pe_sh, out_sm, out_sh;
+  uint32_t q_sm, q_sh, pe_sm, pe_sh, out_sm, out_sh;
   int M;
   int H;
 };

@@ -37,6 +37,8 @@
 // fp32 value of each E4M3 byte, the product with 2^(S-127) is exact, and the
 // top half of that fp32 is its exact bf16. The bf16 MFMA then forms exact
 // products with q_nope, as the pages' exact dequantization requires.
+#include <type_traits>
+
 #include "mlaq.h"
 #include "mlaq_internal.h"
 
@@ -128,6 +130,14 @@ __device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[(RB + 3
   }
 }
 
+// Base pointer + 32-bit byte offset: a uniform base and a zero-extended
+// 32-bit offset let the compiler use the SGPR-base form of global memory ops.
+template <typename T, typename P>
+__device__ __forceinline__ T* at_byte(P* base, uint32_t byte_off) {
+  return reinterpret_cast<T*>(reinterpret_cast<typename std::conditional<std::is_const<P>::value, const uint8_t,
+                                                                          uint8_t>::type*>(base) + byte_off);
+}
+
 // Block -> tile. The dispatcher deals blocks round-robin over the 8 XCDs
 // (block b runs on XCD b % 8), and each XCD has its own L2. Tiles are numbered
 // head-major (tile = h * NCT + column tile), and XCD x is given the
@@ -175,22 +185,24 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   const bool has_pe = pe_chunk < M * (kRope / 8);
   const int pe_x = has_pe ? pe_chunk : 0; // loads stay unconditional (no branch, no early wait)
   const int pe_m = pe_x >> 3, pe_c = pe_x & 7;
-  const u32x4_t pe_v = *reinterpret_cast<const u32x4_t*>(a.q_pe + pe_m * a.pe_sm + h * a.pe_sh + 8 * pe_c);
+  const uint32_t pe_off = __umul24(pe_m, a.pe_sm) + __umul24(h, a.pe_sh) + 8 * pe_c;
+  const u32x4_t pe_v = *at_byte<const u32x4_t>(a.q_pe, 2 * pe_off);
   __builtin_amdgcn_sched_barrier(0); // keep the q_pe load ahead of the weight loads
 
   // 2. Weight rows (the bulk of the bytes), all requested up front.
   uint32_t wr[8][D];
   {
-    const uint8_t* base =
-        static_cast<const uint8_t*>(a.w) + ((size_t(h) * K + k0) * kLatent + col) * ESZ;
+    const uint32_t off = ((uint32_t(h) * K + k0) * kLatent + col) * ESZ; // < 2^22
+    __builtin_assume(off < (1u << 22));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) load_row<RB>(base + size_t(r) * kLatent * ESZ, wr[r]);
+    for (int r = 0; r < 8; ++r)
+      load_row<RB>(static_cast<const uint8_t*>(a.w) + (off + uint32_t(r) * kLatent * ESZ), wr[r]);
   }
   uint32_t sc[8];
   if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
-    const uint8_t* sb = a.w_scales + (size_t(h) * K + k0) * kScalesPerRow + col / kMxBlock;
+    const uint32_t off = (uint32_t(h) * K + k0) * kScalesPerRow + col / kMxBlock;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sc[r] = sb[r * kScalesPerRow];
+    for (int r = 0; r < 8; ++r) sc[r] = a.w_scales[off + uint32_t(r) * kScalesPerRow];
   }
 
   // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7. Rows past M read
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + j;
     const int mc = m < M ? m : 0;
-    qa[t] = *reinterpret_cast<const u32x4_t*>(a.q_nope + mc * a.q_sm + h * a.q_sh + k0);
+    qa[t] = *at_byte<const u32x4_t>(a.q_nope, 2 * (__umul24(mc, a.q_sm) + __umul24(h, a.q_sh) + k0));
   }
   __builtin_amdgcn_sched_barrier(0); // all loads are in flight before any wait
 
@@ -213,9 +225,9 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     rqs = 1.0f / qs;
   }
   if (has_pe) {
-    const int64_t o = pe_m * a.out_sm + h * a.out_sh + kLatent + 8 * pe_c;
+    const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
     if constexpr (OF == MLAQ_OUT_BF16) {
-      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + o) = pe_v;
+      *at_byte<u32x4_t>(a.out, 2 * o) = pe_v;
     } else {
       float x[8];
 #pragma unroll
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
       u32x2_t v;
       v[0] = e4m3x4_satfinite(x[0], x[1], x[2], x[3]);
       v[1] = e4m3x4_satfinite(x[4], x[5], x[6], x[7]);
-      *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + o) = v;
+      *at_byte<u32x2_t>(a.out, o) = v;
     }
   }
   __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
@@ -300,15 +312,15 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
-    const int64_t o = m * a.out_sm + h * a.out_sh + c0 + 4 * cg;
+    const uint32_t o = __umul24(m, a.out_sm) + __umul24(h, a.out_sh) + c0 + 4 * cg;
     const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
     const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
     if constexpr (OF == MLAQ_OUT_BF16) {
-      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + o) = u32x2_t{b01, b23};
+      *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{b01, b23};
     } else {
       const float y0 = __uint_as_float(b01 << 16), y1 = __uint_as_float(b01 & 0xffff0000u);
       const float y2 = __uint_as_float(b23 << 16), y3 = __uint_as_float(b23 & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.out) + o) =
+      *at_byte<uint32_t>(a.out, o) =
           e4m3x4_satfinite(div_rn(y0, qs, rqs), div_rn(y1, qs, rqs), div_rn(y2, qs, rqs), div_rn(y3, qs, rqs));
     }
   }
