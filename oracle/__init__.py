@@ -76,6 +76,8 @@ def _declare(lib):
     P = ctypes.c_void_p
     lib.mlaq_oracle_run.restype = ctypes.c_int
     lib.mlaq_oracle_run.argtypes = [P, P, P, P, ctypes.c_float, P] + [ctypes.c_int] * 7 + [P, P, P, ctypes.c_int]
+    lib.mlaq_oracle_uv_run.restype = ctypes.c_int
+    lib.mlaq_oracle_uv_run.argtypes = [P, P, P, P] + [ctypes.c_int] * 5 + [P, P]
     lib.mlaq_oracle_qscale.restype = ctypes.c_float
     lib.mlaq_oracle_qscale.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t]
     for name in ("mlaq_oracle_bf16_round", "mlaq_oracle_e4m3_encode", "mlaq_oracle_e4m3_decode",
@@ -150,6 +152,42 @@ def mla_query(q_nope, q_pe, w, w_scales=None, q_scale=None, *, weight_format=WEI
     res = {"out": out}
     if diagnostics:
         res.update(acc=acc, s_abs=sabs, ref64=ref)
+    return res
+
+
+def uv_projection(x, w, w_scales=None, *, weight_format=WEIGHT_BF16, diagnostics=True, lib_path=None):
+    """V up-projection on host arrays: ``x`` uint16 (bf16) ``[M,H,C]``, ``w``
+    uint16 (bf16) or uint8 (E4M3) ``[H,V,C]`` (one latent row per value
+    column), ``w_scales`` uint8 (E8M0) ``[H,V,C/32]`` for MXFP8. Returns
+    ``out`` uint16 ``[M,H,V]`` and, with diagnostics, ``acc`` (fp32) and
+    ``s_abs`` (fp64 sum of |x w|). The arithmetic is ``mlaq_oracle_uv_run``."""
+    lib = _load(lib_path)
+    x = _c(x, np.uint16)
+    M, H, C = x.shape
+    if weight_format == WEIGHT_BF16:
+        w = _c(w, np.uint16)
+        if w_scales is not None:
+            raise OracleError("BF16 weights take no scales")
+    else:
+        w = _c(w, np.uint8)
+        w_scales = _c(w_scales, np.uint8)
+    Hw, V, Cw = w.shape
+    if (Hw, Cw) != (H, C):
+        raise OracleError("W_UV shape must be [H,V,C]")
+    if weight_format == WEIGHT_MXFP8 and w_scales.shape != (H, V, C // MX_BLOCK):
+        raise OracleError("scale shape must be [H,V,C/32]")
+    out = np.zeros((M, H, V), np.uint16)
+    acc = sabs = None
+    if diagnostics:
+        acc = np.zeros((M, H, V), np.float32)
+        sabs = np.zeros((M, H, V), np.float64)
+    rc = lib.mlaq_oracle_uv_run(_ptr(x), _ptr(w), _ptr(w_scales), _ptr(out), M, H, C, V, int(weight_format),
+                                _ptr(acc), _ptr(sabs))
+    if rc != 0:
+        raise OracleError(f"mlaq_oracle_uv_run failed with status {rc}")
+    res = {"out": out}
+    if diagnostics:
+        res.update(acc=acc, s_abs=sabs)
     return res
 
 

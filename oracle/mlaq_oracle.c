@@ -327,3 +327,67 @@ void mlaq_oracle_e4m3_decode(const uint8_t* in, double* out, size_t n) {
 void mlaq_oracle_e8m0_decode(const uint8_t* in, double* out, size_t n) {
   for (size_t i = 0; i < n; ++i) out[i] = e8m0_to_f64(in[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* V up-projection (the step after MLA decode attention)                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every token m < M, head h < H and value column v < V:
+ *
+ *   acc[m,h,v] = sum over c = 0..C-1 (ascending) of x[m,h,c] * W_UV[h,v,c]
+ *                accumulated in fp32, each product formed exactly
+ *   out[m,h,v] = bf16 round-to-nearest-even of acc
+ *
+ * x is the attention output in the latent space, bf16 [M,H,C]; W_UV is stored
+ * as the checkpoint holds it, one row of C latent values per value column,
+ * bf16 or E4M3 [H,V,C], with MXFP8 scales along the latent (reduction) axis,
+ * one E8M0 byte per 32 contiguous c of each row: [H,V,C/32]. (The pages name
+ * this projection -- vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query
+ * assembly", "Layout and topology behavior" and "Safety scope and PR 173" --
+ * without its shapes; C = 512 latent and V = 128 value dims are the readings.)
+ * Same codecs and accumulation as the query projection above. Returns 0, or 1
+ * on bad sizes/formats, 2 on missing buffers, 3 on host allocation failure.
+ */
+int mlaq_oracle_uv_run(const uint16_t* x, const void* w, const uint8_t* w_scales, uint16_t* out, int M, int H,
+                       int C, int V, int weight_format, float* acc_out, double* sabs_out) {
+  if (M < 0 || H < 0 || C < ORACLE_MX_BLOCK || C % ORACLE_MX_BLOCK || V < 1) return 1;
+  if (weight_format != ORACLE_WEIGHT_BF16 && weight_format != ORACLE_WEIGHT_MXFP8) return 1;
+  if (M == 0 || H == 0) return 0;
+  if (!x || !w || !out || (weight_format == ORACLE_WEIGHT_MXFP8 && !w_scales)) return 2;
+  double* wdq = (double*)malloc(sizeof(double) * (size_t)V * C);
+  if (!wdq) return 3;
+  for (int h = 0; h < H; ++h) {
+    /* Step 1: dequantize this head's W_UV[h] (exact in double). */
+    for (int v = 0; v < V; ++v)
+      for (int c = 0; c < C; ++c) {
+        size_t idx = ((size_t)h * V + v) * C + c;
+        if (weight_format == ORACLE_WEIGHT_BF16) {
+          wdq[(size_t)v * C + c] = (double)bf16_to_f32(((const uint16_t*)w)[idx]);
+        } else {
+          uint8_t p = ((const uint8_t*)w)[idx];
+          uint8_t s = w_scales[((size_t)h * V + v) * (C / ORACLE_MX_BLOCK) + c / ORACLE_MX_BLOCK];
+          wdq[(size_t)v * C + c] = e4m3_to_f64(p) * e8m0_to_f64(s);
+        }
+      }
+    /* Step 2: contract over c in ascending order (fp32), step 3: round. */
+    for (int m = 0; m < M; ++m) {
+      const uint16_t* xr = x + ((size_t)m * H + h) * C;
+      for (int v = 0; v < V; ++v) {
+        float acc = 0.0f;
+        double sabs = 0.0;
+        for (int c = 0; c < C; ++c) {
+          double p = (double)bf16_to_f32(xr[c]) * wdq[(size_t)v * C + c];
+          acc = acc + (float)p;
+          sabs += fabs(p);
+        }
+        size_t o = ((size_t)m * H + h) * V + v;
+        if (acc_out) acc_out[o] = acc;
+        if (sabs_out) sabs_out[o] = sabs;
+        out[o] = f32_to_bf16_rne(acc);
+      }
+    }
+  }
+  free(wdq);
+  return 0;
+}

@@ -361,3 +361,88 @@ def check_e4m3_double_rounding(lib=None):
 
 
 ALL_CHECKS.insert(9, check_e4m3_double_rounding)
+
+
+# --------------------------------------------------------------------------
+# V up-projection oracle
+# --------------------------------------------------------------------------
+
+def check_uv_identity(lib=None, H=16, M=3):
+    """W_UV[h,v,c] = 1 iff c = v + 128 (h mod 4): out[m,h,v] = x[m,h,v + 128 (h mod 4)]
+    bit for bit (BF16 weights, and MXFP8 payload 1.0 with per-row 2^e scales)."""
+    rng = _rng(51)
+    x = _rand_bf16(rng, (M, H, 512))
+    w = np.zeros((H, 128, 512), np.uint16)
+    w8 = np.zeros((H, 128, 512), np.uint8)
+    s8 = np.zeros((H, 128, 16), np.uint8)
+    e = np.zeros((H, 128), np.int64)
+    for h in range(H):
+        v = np.arange(128)
+        w[h, v, v + 128 * (h % 4)] = BF16_ONE
+        w8[h, v, v + 128 * (h % 4)] = 0x38
+        e[h] = (h + 3 * v) % 7 - 5
+        s8[h] = (127 + e[h])[:, None]
+    out = oracle.uv_projection(x, w, lib_path=lib)["out"]
+    want = np.stack([x[:, h, 128 * (h % 4):128 * (h % 4) + 128] for h in range(H)], axis=1)
+    assert np.array_equal(out, want), "UV identity weights do not select x bit-exactly"
+    out8 = oracle.uv_projection(x, w8, s8, weight_format=1, lib_path=lib)["out"]
+    want8 = np.stack([bf16_bits((_f32(want[:, h, :]).astype(np.float64) * np.ldexp(1.0, e[h])[None, :])
+                                .astype(np.float32)) for h in range(H)], axis=1)
+    assert np.array_equal(out8, want8), "UV MXFP8 identity (1.0 x 2^e) not exact"
+
+
+def check_uv_scale_closed_form(lib=None, H=8, M=2):
+    """Payload 1.0 everywhere, E8M0 byte 127 - ((h+v+j) mod 9) for latent group
+    j = c/32, x = 2^-(c mod 4): an exact integer count of 2^-11 units."""
+    w = np.full((H, 128, 512), 0x38, np.uint8)
+    hh, vv, jj = np.meshgrid(np.arange(H), np.arange(128), np.arange(16), indexing="ij")
+    s = (127 - (hh + vv + jj) % 9).astype(np.uint8)
+    xk = np.array([2.0 ** -(c % 4) for c in range(512)], np.float32)
+    x = np.broadcast_to(bf16_bits(xk), (M, H, 512)).copy()
+    out = oracle.uv_projection(x, w, s, weight_format=1, lib_path=lib)["out"]
+    units = np.zeros((H, 128), np.int64)
+    for h in range(H):
+        for v in range(128):
+            units[h, v] = sum(1 << (11 - (c % 4) - ((h + v + c // 32) % 9)) for c in range(512))
+    want = bf16_bits((units.astype(np.float64) / 2048.0).astype(np.float32))
+    for m in range(M):
+        assert np.array_equal(out[m], want), "UV E8M0 scale applied to the wrong (v, c) group"
+
+
+GAMMA_512 = (512 * 2.0 ** -24) / (1 - 512 * 2.0 ** -24)
+
+
+def check_uv_brute_force(lib=None):
+    """H, M in 1..2, C = 64, V = 8: the fp32 accumulator within gamma_C * sum|x w|
+    of the exact rational sum, the bf16 result within one ulp of it."""
+    C, V = 64, 8
+    gamma = (C * 2.0 ** -24) / (1 - C * 2.0 ** -24)
+    for wf in (0, 1):
+        for H in (1, 2):
+            for M in (1, 2):
+                rng = _rng(700 + 10 * H + M + 50 * wf)
+                x = _rand_bf16(rng, (M, H, C))
+                if wf == 0:
+                    w = _rand_bf16(rng, (H, V, C), std=C ** -0.5)
+                    s = None
+                    wval = _f32(w).astype(np.float64)
+                else:
+                    w = e4m3_bits(rng.standard_normal((H, V, C)).astype(np.float32) * 0.1)
+                    s = (127 + rng.integers(-8, 1, (H, V, C // MX_BLOCK))).astype(np.uint8)
+                    dec = torch.from_numpy(w.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                    wval = dec * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(MX_BLOCK, axis=2)
+                res = oracle.uv_projection(x, w, s, weight_format=wf, lib_path=lib)
+                xv = _f32(x).astype(np.float64)
+                for m in range(M):
+                    for h in range(H):
+                        for v in range(V):
+                            terms = [Fraction(xv[m, h, c]) * Fraction(wval[h, v, c]) for c in range(C)]
+                            exact = sum(terms, Fraction(0))
+                            sabs = sum(abs(t) for t in terms)
+                            acc = Fraction(float(res["acc"][m, h, v]))
+                            assert abs(acc - exact) <= Fraction(gamma) * sabs, (wf, H, M, m, h, v)
+                            y = float(_f32(res["out"][m, h, v:v + 1])[0])
+                            assert abs(Fraction(y) - exact) <= Fraction(float(_ulp_bf16(float(exact)))), (m, h, v)
+
+
+ALL_CHECKS.extend([check_uv_identity, check_uv_scale_closed_form, check_uv_brute_force])

@@ -9,7 +9,10 @@ import oracle_pins as pins
 
 MUTANTS = {
     "drop_last_k_term": ("k < K; ++k) {\n        double p", "k < K - 1; ++k) {\n        double p"),
-    "wrong_sign": ("acc = acc + (float)p;", "acc = acc - (float)p;"),
+    "wrong_sign": ("acc = acc + (float)p;\n        sabs += fabs(p);\n        ref += p;",
+                   "acc = acc - (float)p;\n        sabs += fabs(p);\n        ref += p;"),
+    "uv_wrong_sign": ("acc = acc + (float)p;\n          sabs += fabs(p);\n        }",
+                      "acc = acc - (float)p;\n          sabs += fabs(p);\n        }"),
     "scale_index_by_k": ("+ n / ORACLE_MX_BLOCK];", "+ k / ORACLE_MX_BLOCK];"),
     "q_nope_as_HMK": ("j->q_nope + ((size_t)m * H + h) * K", "j->q_nope + ((size_t)h * j->M + m) * K"),
     "weight_as_HNK": ("size_t idx = ((size_t)h * j->K + k) * j->N + n;",
@@ -23,6 +26,10 @@ MUTANTS = {
     "multiply_by_q_scale": ("f32_to_e4m3_satfinite(v / q_scale)", "f32_to_e4m3_satfinite(v * q_scale)"),
     "e4m3_without_bf16_step": ("to_e4m3_out(bf16_to_f32(y), j->q_scale)", "to_e4m3_out(acc, j->q_scale)"),
     "q_pe_unscaled": ("to_e4m3_out(bf16_to_f32(pe[r]), j->q_scale)", "to_e4m3_out(bf16_to_f32(pe[r]), 1.0f)"),
+    "uv_scale_indexed_by_v": ("* (C / ORACLE_MX_BLOCK) + c / ORACLE_MX_BLOCK];",
+                              "* (C / ORACLE_MX_BLOCK) + v % (C / ORACLE_MX_BLOCK)];"),
+    "uv_weight_as_HCV": ("size_t idx = ((size_t)h * V + v) * C + c;", "size_t idx = ((size_t)h * C + c) * V + v;"),
+    "uv_drop_last_c": ("for (int c = 0; c < C; ++c) {\n          double p", "for (int c = 0; c < C - 1; ++c) {\n          double p"),
     "projection_offset_by_one": ("((uint16_t*)j->out)[orow + n] = y;", "((uint16_t*)j->out)[orow + (n + 1) % N] = y;"),
 }
 
