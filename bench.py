@@ -25,6 +25,7 @@ Printed JSON line (stdout, one line):
   pages_shape the pages' own workload (K=192, H=8, M=1, BF16, 78 layers,
               cold) fused vs staged per layer, and their AB/BA graph-replay
               comparison over H=8/11/16 x M=1/4/32
+  uv_projection the V up-projection that follows attention, same step form
   staged      the staged path (torch.bmm + copies + E4M3 quantization) of the
               same step on the same GPU
   cpu_baseline the CPU oracle timed on this host over a bounded sample of the
@@ -62,6 +63,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true")
     p.add_argument("--no-pages-shape", action="store_true")
+    p.add_argument("--no-uv", action="store_true")
     p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -396,6 +398,75 @@ def pages_shape_leg(torch, mq, wl, args):
             "ab_ba_graph_replay": {"samples_per_shape": args.ab_samples, "shapes": ab}}
 
 
+def uv_leg(torch, mq, wl, args):
+    """V up-projection in the same decode-step form: 64 layers (BF16 / MXFP8
+    W_UV alternating), H=16, M=32, one hipGraph per step, 6 rotated weight
+    copies (cold), against the staged torch.bmm + copy. Inputs: x ~ N(0,1)
+    bf16 [M,H,512]; W_UV ~ N(0, 1/sqrt(512)) as bf16 or E4M3 [H,128,512] with
+    E8M0 exponents U{-8..0} along the latent; seeds 100 * 1005 + layer."""
+    Hh, M, L, C = H, M_STEP, LAYERS, COPIES
+    stream = torch.cuda.Stream()
+    lay = []
+    for l in range(L):
+        wf = mq.MLAQ_WEIGHT_BF16 if l % 2 == 0 else mq.MLAQ_WEIGHT_MXFP8
+        rng = np.random.Generator(np.random.PCG64(100 * 1005 + l))
+        x = wl.bf16_bits(rng.standard_normal((M, Hh, 512), dtype=np.float32))
+        std = np.float32(512 ** -0.5)
+        if wf == mq.MLAQ_WEIGHT_BF16:
+            w, sc = wl.bf16_bits(rng.standard_normal((Hh, 128, 512), dtype=np.float32) * std), None
+        else:
+            w = wl.e4m3_bits(rng.standard_normal((Hh, 128, 512), dtype=np.float32) * std)
+            sc = (127 + rng.integers(-8, 1, size=(Hh, 128, 16))).astype(np.uint8)
+        lay.append({"wf": wf, "x": dev_bf16(torch, x), "w": w, "s": sc,
+                    "out": torch.empty((M, Hh, 128), dtype=torch.bfloat16, device="cuda")})
+    copies = [[(dev_bf16(torch, d["w"]) if d["wf"] == mq.MLAQ_WEIGHT_BF16 else dev_u8(torch, d["w"]),
+                None if d["s"] is None else dev_u8(torch, d["s"])) for d in lay] for _ in range(C)]
+    for wf in (mq.MLAQ_WEIGHT_BF16, mq.MLAQ_WEIGHT_MXFP8):
+        mq.mlaq_uv_prewarm(Hh, [M], wf)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(C):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                for d, (w, sc) in zip(lay, copies[c]):
+                    mq.mlaq_uv_run(d["x"], w, sc, d["out"], d["wf"])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=L) * 1e3
+    nbytes = sum(128 * 512 * Hh * (2 if d["wf"] == 0 else 1) + (0 if d["s"] is None else Hh * 128 * 16)
+                 + M * Hh * 512 * 2 + M * Hh * 128 * 2 for d in lay)
+    # staged: materialized bf16 W_UV^T [H,512,128] (contiguous) + bmm + copy
+    staged_w = []
+    for c in range(C):
+        row = []
+        for d, (w, sc) in zip(lay, copies[c]):
+            wb = w if sc is None else (w.view(torch.float8_e4m3fn).float() *
+                                       torch.exp2(sc.float() - 127.0).repeat_interleave(32, dim=2)).to(torch.bfloat16)
+            row.append(wb.transpose(1, 2).contiguous())
+        staged_w.append(row)
+    sgraphs = []
+    for c in range(C):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for d, wt in zip(lay, staged_w[c]):
+                    t = torch.bmm(d["x"].transpose(0, 1).contiguous(), wt)
+                    d["out"].copy_(t.transpose(0, 1))
+        sgraphs.append(g)
+    torch.cuda.synchronize()
+    s_us = time_graphs(torch, sgraphs, args.steps, args.warmup, per_step_units=L) * 1e3
+    gbs = nbytes / L / (us * 1e-6) / 1e9
+    log(f"[bench] UV projection (H=16, M=32, 64 cold layers): fused {us:.3f} us/layer ({gbs:.1f} GB/s), "
+        f"staged {s_us:.3f} us/layer")
+    del graphs, sgraphs, staged_w, copies
+    torch.cuda.synchronize()
+    return {"workload": "V up-projection, 64 layers (BF16/MXFP8 W_UV alternating), H=16, M=32, one hipGraph "
+                        "per step, 6 rotated weight copies (cold)",
+            "us_per_layer": round(us, 4), "gbs": round(gbs, 1), "staged_us_per_layer": round(s_us, 4),
+            "bytes_per_step": nbytes}
+
+
 def cpu_baseline_leg(wl, layers, budget_s):
     """The CPU oracle on the step's layers, cycling through them until the
     time budget is spent (the oracle as it stands, threaded over heads)."""
@@ -483,6 +554,7 @@ def main():
     step = decode_step_leg(torch, mq, wl, args)
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
     pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
+    uv = None if args.no_uv else uv_leg(torch, mq, wl, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
@@ -516,6 +588,7 @@ def main():
         "floors": step["floors"],
         "per_call": per_call,
         "pages_shape": pages,
+        "uv_projection": uv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -56,6 +56,7 @@ extern "C" {
 #define MLAQ_LATENT_DIM 512
 #define MLAQ_ROPE_DIM 64
 #define MLAQ_MAX_M 32
+#define MLAQ_V_DIM 128 /* value width of the UV projection */
 
 /*
  * mlaq_plan_supported -- the pure capability gate (no HIP call).
@@ -160,6 +161,31 @@ typedef struct mlaq_run_args {
 } mlaq_run_args;
 
 int mlaq_run_ex(const mlaq_run_args* args, void* stream);
+
+/*
+ * V up-projection, the step after MLA decode attention (vLLM page, "Layout and
+ * topology behavior" and "Safety scope and PR 173", where the UV projection
+ * sits beside the fused query path): for every token m < M and head h < H,
+ *
+ *   out[m,h,v] = bf16_rne( sum_{c<512} x[m,h,c] * W_UV[h,v,c] )   fp32 accumulation, v < 128
+ *
+ *   x           bf16 [M,H,512] (attention output in the latent space), contiguous
+ *   w_uv        bf16 or E4M3FN bytes [H,128,512]: one latent row per value
+ *               column (the checkpoint's layout), latent contiguous
+ *   w_uv_scales E8M0 [H,128,16]: byte [h,v,j] scales latent 32j..32j+31 of row v;
+ *               required for MXFP8, must be NULL for BF16 weights
+ *   out         bf16 [M,H,128], contiguous
+ * All 16-byte aligned; out must not overlap an input. Sizes: latent 512,
+ * value 128, H in {8, 11, 16}, M in 0..32 (0: no-op). Same status codes,
+ * asynchrony, graph-capturability and determinism as mlaq_run.
+ */
+int mlaq_uv_plan_supported(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format,
+                           const char* arch);
+int mlaq_uv_can_implement(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format,
+                          int device);
+int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_format, int device);
+int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
+                int weight_format, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the thread's next mlaq_* call. */

@@ -17,7 +17,10 @@ The entry points carry the C names (see ``include/mlaq.h``):
 * ``mlaq_run``            -- one fused call: ``[M,H,576]`` output with q_pe
   appended in the same launch (sparkinfer page, "What"; vLLM page, "What");
 * ``mlaq_run_ex``         -- the same with strided views (a head-major q_nope,
-  a pitched output workspace) and nope width 128 or 192.
+  a pitched output workspace) and nope width 128 or 192;
+* ``mlaq_uv_*``           -- the V up-projection that follows attention:
+  ``out[m,h,:128] = x[m,h,:512] . W_UV[h]`` (vLLM page, "Layout and topology
+  behavior": the UV projection beside the fused query path).
 """
 
 from __future__ import annotations
@@ -35,6 +38,7 @@ MLAQ_OUT_BF16, MLAQ_OUT_E4M3 = 0, 1
 MLAQ_OK, MLAQ_ERR_UNSUPPORTED, MLAQ_ERR_INVALID_ARG, MLAQ_ERR_DEVICE = 0, 1, 2, 3
 NOPE_DIM, LATENT_DIM, ROPE_DIM, MAX_M = 128, 512, 64, 32
 NOPE_DIM_GLM = 192
+V_DIM = 128
 ROW = LATENT_DIM + ROPE_DIM
 MX_BLOCK = 32
 
@@ -81,6 +85,14 @@ def library() -> ctypes.CDLL:
         lib.mlaq_run.restype = I
         lib.mlaq_run_ex.argtypes = [ctypes.POINTER(RunArgs), P]
         lib.mlaq_run_ex.restype = I
+        lib.mlaq_uv_plan_supported.argtypes = [I] * 5 + [ctypes.c_char_p]
+        lib.mlaq_uv_plan_supported.restype = I
+        lib.mlaq_uv_can_implement.argtypes = [I] * 6
+        lib.mlaq_uv_can_implement.restype = I
+        lib.mlaq_uv_prewarm.argtypes = [I, P, I, I, I]
+        lib.mlaq_uv_prewarm.restype = I
+        lib.mlaq_uv_run.argtypes = [P, P, P, P, I, I, I, P]
+        lib.mlaq_uv_run.restype = I
         lib.mlaq_last_error.argtypes = []
         lib.mlaq_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -232,3 +244,45 @@ def fused_query(q_nope, q_pe, w, w_scales=None, q_scale=None, out_dtype: int = M
         out = torch.empty((M, H, ROW), dtype=dt, device=q_nope.device)
     mlaq_run(q_nope, q_pe, w, w_scales, q_scale, out, wf, out_dtype)
     return out
+
+
+def mlaq_uv_plan_supported(num_heads: int, max_m: int, latent_dim: int = LATENT_DIM, v_dim: int = V_DIM,
+                           weight_format: int = MLAQ_WEIGHT_MXFP8, arch: str = "gfx950") -> int:
+    """Status of the pure UV-projection gate for an architecture name."""
+    return library().mlaq_uv_plan_supported(num_heads, max_m, latent_dim, v_dim, weight_format,
+                                            arch.encode() if arch is not None else None)
+
+
+def mlaq_uv_can_implement(num_heads: int, max_m: int, latent_dim: int = LATENT_DIM, v_dim: int = V_DIM,
+                          weight_format: int = MLAQ_WEIGHT_MXFP8, device=None) -> bool:
+    return bool(library().mlaq_uv_can_implement(num_heads, max_m, latent_dim, v_dim, weight_format,
+                                                _device_index(device)))
+
+
+def mlaq_uv_prewarm(num_heads: int, m_regimes, weight_format: int, device=None) -> None:
+    regs = list(m_regimes)
+    arr = (ctypes.c_int * max(1, len(regs)))(*regs)
+    _check(library().mlaq_uv_prewarm(num_heads, arr, len(regs), weight_format, _device_index(device)))
+
+
+def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor | None, out: torch.Tensor,
+                weight_format: int, stream: torch.cuda.Stream | None = None) -> None:
+    """V up-projection: x bf16 [M,H,512], w_uv bf16 or float8_e4m3fn/uint8
+    [H,128,512] (latent contiguous), w_uv_scales uint8/float8_e8m0fnu
+    [H,128,16] (MXFP8) or None, out bf16 [M,H,128]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [M,H,512]")
+    M, H = int(x.shape[0]), int(x.shape[1])
+    dev = x.device
+    _expect(x, "x", torch.bfloat16, (M, H, LATENT_DIM), dev)
+    wdt = torch.bfloat16 if weight_format == MLAQ_WEIGHT_BF16 else (
+        w_uv.dtype if w_uv.dtype in (torch.float8_e4m3fn, torch.uint8) else torch.float8_e4m3fn)
+    _expect(w_uv, "w_uv", wdt, (H, V_DIM, LATENT_DIM), dev)
+    if w_uv_scales is not None:
+        _expect(w_uv_scales, "w_uv_scales",
+                w_uv_scales.dtype if w_uv_scales.dtype in (torch.uint8, torch.float8_e8m0fnu) else torch.uint8,
+                (H, V_DIM, LATENT_DIM // MX_BLOCK), dev)
+    _expect(out, "out", torch.bfloat16, (M, H, V_DIM), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(library().mlaq_uv_run(_ptr(x), _ptr(w_uv), _ptr(w_uv_scales), _ptr(out), M, H, weight_format,
+                                 ctypes.c_void_p(s.cuda_stream)))

@@ -249,6 +249,85 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
   return mlaq_run_ex(&a, stream);
 }
 
+int mlaq_uv_plan_supported(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format, const char* arch) {
+  clear_error();
+  if (!arch) return fail(MLAQ_ERR_INVALID_ARG, "arch is NULL");
+  if (!known_weight_format(weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", weight_format);
+  if (!is_gfx950(arch)) return fail(MLAQ_ERR_UNSUPPORTED, "device architecture '%s' is not gfx950", arch);
+  if (!supported_heads(num_heads)) return fail(MLAQ_ERR_UNSUPPORTED, "num_heads=%d not in {8, 11, 16}", num_heads);
+  if (max_m < 1 || max_m > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "max_m=%d outside 1..32", max_m);
+  if (latent_dim != MLAQ_LATENT_DIM || v_dim != MLAQ_V_DIM)
+    return fail(MLAQ_ERR_UNSUPPORTED, "dims (latent %d, v %d) are not (512, 128)", latent_dim, v_dim);
+  return MLAQ_OK;
+}
+
+int mlaq_uv_can_implement(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format, int device) {
+  clear_error();
+  const char* arch = nullptr;
+  if (device_arch(device, &arch) != MLAQ_OK) return 0;
+  return mlaq_uv_plan_supported(num_heads, max_m, latent_dim, v_dim, weight_format, arch) == MLAQ_OK;
+}
+
+int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_format, int device) {
+  clear_error();
+  if (n_regimes < 0 || (n_regimes > 0 && !m_regimes))
+    return fail(MLAQ_ERR_INVALID_ARG, "m_regimes is NULL or n_regimes < 0");
+  const char* arch = nullptr;
+  int st = device_arch(device, &arch);
+  if (st != MLAQ_OK) return st;
+  for (int i = 0; i < n_regimes; ++i) {
+    st = mlaq_uv_plan_supported(num_heads, m_regimes[i], MLAQ_LATENT_DIM, MLAQ_V_DIM, weight_format, arch);
+    if (st != MLAQ_OK) return st;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+    hipFuncAttributes attr;
+    if (e == hipSuccess) e = hipFuncGetAttributes(&attr, mlaq::uv_kernel_for(weight_format, m_regimes[i] <= 16 ? 1 : 2));
+    if (cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
+  }
+  return MLAQ_OK;
+}
+
+int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H, int weight_format,
+                void* stream) {
+  clear_error();
+  if (!known_weight_format(weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", weight_format);
+  if (!supported_heads(H)) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d not in {8, 11, 16}", H);
+  if (M < 0 || M > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "M=%d outside 0..32", M);
+  if (M == 0) return MLAQ_OK;
+  if (!x || !w_uv || !out) return fail(MLAQ_ERR_INVALID_ARG, "x, w_uv and out must be non-NULL");
+  if (weight_format == MLAQ_WEIGHT_MXFP8 && !w_uv_scales) return fail(MLAQ_ERR_INVALID_ARG, "MXFP8 weights need w_uv_scales");
+  if (weight_format == MLAQ_WEIGHT_BF16 && w_uv_scales)
+    return fail(MLAQ_ERR_INVALID_ARG, "BF16 weights take no w_uv_scales (pass NULL)");
+  if (!aligned(x, 16) || !aligned(w_uv, 16) || !aligned(out, 16))
+    return fail(MLAQ_ERR_INVALID_ARG, "x, w_uv and out must be 16-byte aligned");
+  const size_t mh = size_t(M) * size_t(H);
+  const size_t out_bytes = mh * mlaq::kValue * 2;
+  const size_t esz_w = weight_format == MLAQ_WEIGHT_BF16 ? 2 : 1;
+  if (overlaps(out, out_bytes, x, mh * mlaq::kLatent * 2) ||
+      overlaps(out, out_bytes, w_uv, size_t(H) * mlaq::kValue * mlaq::kLatent * esz_w) ||
+      overlaps(out, out_bytes, w_uv_scales, size_t(H) * mlaq::kValue * (mlaq::kLatent / mlaq::kMxBlock)))
+    return fail(MLAQ_ERR_INVALID_ARG, "out overlaps an input buffer");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  const char* arch = nullptr;
+  int st = device_arch(device, &arch);
+  if (st != MLAQ_OK) return st;
+  st = mlaq_uv_plan_supported(H, M, MLAQ_LATENT_DIM, MLAQ_V_DIM, weight_format, arch);
+  if (st != MLAQ_OK) return st;
+  const void* fn = mlaq::uv_kernel_for(weight_format, M <= 16 ? 1 : 2);
+  if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
+  dim3 grid, block;
+  mlaq::uv_launch_shape(H, &grid, &block);
+  mlaq::UvArgs ka{static_cast<const uint16_t*>(x), w_uv, static_cast<const uint8_t*>(w_uv_scales), out, M, H};
+  void* kargs[] = {&ka};
+  e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
 const char* mlaq_last_error(void) { return g_err; }
 
 } // extern "C"

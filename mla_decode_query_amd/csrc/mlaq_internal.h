@@ -13,6 +13,7 @@ constexpr int kLatent = 512; // N: projection width
 constexpr int kRope = 64;    // R: appended q_pe width
 constexpr int kRow = kLatent + kRope;
 constexpr int kMxBlock = 32; // E8M0 scale group along n
+constexpr int kValue = 128;  // V: value width of the UV projection
 constexpr int kMaxM = 32;
 constexpr int64_t kMaxStride = int64_t(1) << 24; // elements; keeps kernel offsets 32-bit
 
@@ -42,6 +43,20 @@ struct Variant {
 inline Variant variant_for(int weight_format, int out_dtype, int M, int nope) {
   return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2, nope};
 }
+
+// V up-projection arguments (all contiguous).
+struct UvArgs {
+  const uint16_t* x;       // bf16 [M,H,512]
+  const void* w;           // bf16 or E4M3 [H,128,512] (latent contiguous)
+  const uint8_t* w_scales; // E8M0 [H,128,16] or null
+  void* out;               // bf16 [M,H,128]
+  int M;
+  int H;
+};
+
+// V up-projection kernel for a weight format and M tile count, and its grid.
+const void* uv_kernel_for(int weight_format, int m_tiles);
+void uv_launch_shape(int H, dim3* grid, dim3* block);
 
 // Host function pointer of the kernel for a variant (null if none).
 const void* kernel_for(const Variant& v);

@@ -37,117 +37,14 @@
 // fp32 value of each E4M3 byte, the product with 2^(S-127) is exact, and the
 // top half of that fp32 is its exact bf16. The bf16 MFMA then forms exact
 // products with q_nope, as the pages' exact dequantization requires.
-#include <type_traits>
-
 #include "mlaq.h"
+#include "mlaq_device.h"
 #include "mlaq_internal.h"
 
 namespace mlaq {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kScalesPerRow = kLatent / kMxBlock;
-
-// ---------------------------------------------------------------------------
-// Conversions. bf16 and E4M3 encodes use the gfx950 convert instructions,
-// whose rounding (nearest even) and special values were checked bit for bit
-// against an independent definition of OCP E4M3FN and bf16 rounding on every
-// bf16 pattern, 2.5 M other fp32 values, all E4M3 midpoints and denormals.
-// ---------------------------------------------------------------------------
-
-// Two fp32 -> packed bf16 (low half = lo), round to nearest even, NaN kept
-// (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// The E4M3 conversion saturates: every finite or infinite value past 448 is
-// 448 (NaN stays NaN). v_cvt_pk_fp8_f32 rounds to nearest even into OCP
-// E4M3FN but turns out-of-range values into NaN, hence the clamp.
-__device__ __forceinline__ float clamp448(float v) {
-  return __builtin_isnan(v) ? v : __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
-}
-
-// Four fp32 -> four OCP E4M3FN codes (byte c holds value c), round to nearest
-// even, saturating to +-448.
-__device__ __forceinline__ uint32_t e4m3x4_satfinite(float v0, float v1, float v2, float v3) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v0), clamp448(v1), 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v2), clamp448(v3), r, true);
-  return uint32_t(r);
-}
-
-// Correctly rounded fp32 quotient y / b from rb = RN(1/b): q0 = RN(y * rb)
-// is within one ulp of y / b, the residual y - q0 * b is exact in one FMA,
-// and one FMA correction then gives RN(y / b) (Markstein's correction step).
-// Checked against IEEE division for every finite bf16 y and 40,000 divisors
-// with 2^-64 <= |b| < 2^65. For |y| < 2^-100 the residual can underflow; such
-// quotients are far below the smallest E4M3 step, and q0 carries their sign.
-__device__ __forceinline__ float div_rn(float y, float b, float rb) {
-  const float q0 = y * rb;
-  const float rho = __builtin_fmaf(-q0, b, y);
-  const float q1 = __builtin_fmaf(rho, rb, q0);
-  // q0 is the answer when it is not finite (overflow, NaN) and for tiny or
-  // zero y (which also keeps the sign of a zero quotient).
-  const bool plain = !(__builtin_fabsf(y) >= 0x1p-100f) || !(__builtin_fabsf(q0) <= 0x1.fffffep127f);
-  return plain ? q0 : q1;
-}
-
-// E8M0 scale byte -> 2^(s-127) as fp32 (0xff -> NaN).
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-  const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : s << 23);
-  return __uint_as_float(bits);
-}
-
-// ---------------------------------------------------------------------------
-// Loads
-// ---------------------------------------------------------------------------
-
-// One lane's segment of one k row: RB bytes (2, 4, 8 or 16) into dwords.
-template <int RB>
-__device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[(RB + 3) / 4]) {
-  if constexpr (RB == 2) {
-    d[0] = *reinterpret_cast<const uint16_t*>(p);
-  } else if constexpr (RB == 4) {
-    d[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (RB == 8) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    d[0] = v[0];
-    d[1] = v[1];
-  } else {
-    static_assert(RB == 16, "row segment must be 2, 4, 8 or 16 bytes");
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    d[0] = v[0];
-    d[1] = v[1];
-    d[2] = v[2];
-    d[3] = v[3];
-  }
-}
-
-// Base pointer + 32-bit byte offset: a uniform base and a zero-extended
-// 32-bit offset let the compiler use the SGPR-base form of global memory ops.
-template <typename T, typename P>
-__device__ __forceinline__ T* at_byte(P* base, uint32_t byte_off) {
-  return reinterpret_cast<T*>(reinterpret_cast<typename std::conditional<std::is_const<P>::value, const uint8_t,
-                                                                          uint8_t>::type*>(base) + byte_off);
-}
-
-// Block -> tile. The dispatcher deals blocks round-robin over the 8 XCDs
-// (block b runs on XCD b % 8), and each XCD has its own L2. Tiles are numbered
-// head-major (tile = h * NCT + column tile), and XCD x is given the
-// contiguous tile range [x * n/8, (x+1) * n/8): every head's tiles then sit
-// on one or two XCDs, so its q_nope rows, its q_pe rows and the 128-byte
-// weight lines that neighbouring column tiles share are fetched into one L2
-// instead of eight. Needs n % 8 == 0 (n = H * NCT with NCT >= 8).
-__device__ __forceinline__ int tile_of_block(int b, int nblocks) {
-  return (b & 7) * (nblocks >> 3) + (b >> 3);
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // The fused kernel

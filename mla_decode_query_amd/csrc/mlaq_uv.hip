@@ -1,0 +1,156 @@
+// mlaq_uv.hip -- gfx950 kernel of the V up-projection that follows MLA decode
+// attention: for every token m < M and head h < H,
+//   out[m,h,v] = bf16_rne( sum_{c<512} x[m,h,c] * W_UV[h,v,c] )    fp32 accumulation
+// with x the attention output in the latent space (bf16 [M,H,512]) and W_UV
+// stored as the checkpoint holds it, one 512-wide latent row per value column
+// (bf16 or E4M3 [H,128,512]; MXFP8 scales along the latent, [H,128,16]).
+// (vLLM PR #174 "[GG] Fuse MXFP8 and BF16 MLA query assembly" names this UV
+// projection beside the fused query path, in "Layout and topology behavior"
+// and "Safety scope and PR 173"; the widths are readings.)
+//
+// Layout makes the MFMA easy: the reduction axis (latent c) is contiguous in
+// memory, so a lane's 16-byte load of 8 consecutive c of one value column is
+// directly its B fragment for v_mfma_f32_16x16x32_bf16 (element e of lane
+// j + 16g = row c0 + 8g + e of column j), and the A fragment is the same
+// 8 c of token j's x row. A workgroup (4 waves) owns one head and CB value
+// columns; wave w reduces c in [128w, 128w+128) over four MFMAs, and the
+// four partial tiles are summed through LDS in a fixed order. With CB = 8 the
+// upper 8 MFMA columns repeat the lower 8 (same addresses, so no extra HBM
+// traffic) and are dropped: 16 workgroups per head, 256 at H = 16.
+//
+// MXFP8: a lane loads 8 E4M3 bytes and the one E8M0 byte of their 32-group;
+// v_cvt_pk_f32_fp8 times 2^(S-127) is exact and its top half is the exact
+// bf16, so the MFMA forms exact products as the oracle's dequantization does.
+#include "mlaq.h"
+#include "mlaq_device.h"
+#include "mlaq_internal.h"
+
+namespace mlaq {
+namespace {
+
+using namespace dev;
+
+constexpr int kUvThreads = 256; // 4 waves
+constexpr int kUvScalesPerRow = kLatent / kMxBlock;
+
+template <int WF, int MT, int CB>
+__global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
+  constexpr int NVB = kValue / CB; // column blocks per head
+  constexpr int MROWS = 16 * MT;
+  constexpr int LDW = CB + 4;
+  static_assert(CB == 8 || CB == 16, "8 or 16 value columns per workgroup");
+  __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int h = tile / NVB, vb = tile - h * NVB;
+  const int v = vb * CB + (j % CB); // this lane's value column
+  const int M = a.M, H = a.H;
+  const int cbase = 128 * wave + 8 * g; // + 32 kb: this lane's 8 latent values per MFMA
+
+  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values.
+  u32x4_t wb[4];
+  uint32_t sc[4];
+  if constexpr (WF == MLAQ_WEIGHT_BF16) {
+    const uint32_t off = ((uint32_t(h) * kValue + v) * kLatent + cbase) * 2;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) wb[kb] = *at_byte<const u32x4_t>(a.w, off + 64 * kb);
+  } else {
+    u32x2_t w8[4];
+    const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) w8[kb] = *at_byte<const u32x2_t>(a.w, off + 32 * kb);
+    const uint32_t soff = (uint32_t(h) * kValue + v) * kUvScalesPerRow + cbase / kMxBlock;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = a.w_scales[soff + kb];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) wb[kb] = u32x4_t{w8[kb][0], w8[kb][1], 0u, 0u}; // decoded below
+  }
+
+  // 2. A fragments: token 16t + j, the same 8 latent values per k-block.
+  //    Rows past M read token 0; their MFMA output rows are never stored.
+  u32x4_t xa[MT][4];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + j;
+    const int mc = m < M ? m : 0;
+    const uint32_t off = ((uint32_t(mc) * H + h) * kLatent + cbase) * 2;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) xa[t][kb] = *at_byte<const u32x4_t>(a.x, off + 64 * kb);
+  }
+  __builtin_amdgcn_sched_barrier(0); // every load is in flight before any wait
+
+  // 3. Contraction over this wave's 128 latent values.
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    u32x4_t b = wb[kb];
+    if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
+      // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16 pairs.
+      const float s = e8m0_scale(sc[kb]);
+      u32x4_t d;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int word = int(b[p >> 1]);
+        const f32x2_t f = (p & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        d[p] = __builtin_amdgcn_perm(__float_as_uint(f[1] * s), __float_as_uint(f[0] * s), 0x07060302u);
+      }
+      b = d;
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[t][kb]),
+                                                       __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+  }
+
+  // 4. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of column j.
+  if (j < CB) {
+    float* pw = part + wave * MROWS * LDW;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[(16 * t + 4 * g + r) * LDW + j] = acc[t][r];
+  }
+  __syncthreads();
+
+  // 5. Epilogue: sum the four partials in order, round, store 4 columns.
+  constexpr int GPR = CB / 4;
+  for (int x = tid; x < M * GPR; x += kUvThreads) {
+    const int m = x / GPR, cg = x - m * GPR;
+    const int off = m * LDW + 4 * cg;
+    f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
+    const uint32_t o = (uint32_t(m) * H + h) * kValue + vb * CB + 4 * cg;
+    *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{bf16x2_rne(sum[0], sum[1]), bf16x2_rne(sum[2], sum[3])};
+  }
+}
+
+// Value columns per workgroup: 8 (256 workgroups at H = 16).
+constexpr int kUvCols = 8;
+
+template <int WF, int MT>
+const void* uv_kernel_ptr() {
+  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, MT, kUvCols>);
+}
+
+} // namespace
+
+const void* uv_kernel_for(int weight_format, int m_tiles) {
+  if (weight_format == MLAQ_WEIGHT_BF16) return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2>();
+  if (weight_format == MLAQ_WEIGHT_MXFP8)
+    return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 2>();
+  return nullptr;
+}
+
+void uv_launch_shape(int H, dim3* grid, dim3* block) {
+  *grid = dim3(unsigned(H * (kValue / kUvCols)), 1, 1);
+  *block = dim3(kUvThreads, 1, 1);
+}
+
+} // namespace mlaq

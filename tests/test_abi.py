@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"mlaq_plan_supported", "mlaq_can_implement", "mlaq_prewarm",
-                                         "mlaq_run", "mlaq_run_ex", "mlaq_last_error"}
+                                         "mlaq_run", "mlaq_run_ex", "mlaq_last_error", "mlaq_uv_plan_supported",
+                                         "mlaq_uv_can_implement", "mlaq_uv_prewarm", "mlaq_uv_run"}
 
 
 def test_library_exports_every_declared_function(lib):
@@ -42,7 +43,7 @@ def test_python_constants_match_header():
     defines = dict(re.findall(r"#define\s+(MLAQ_\w+)\s+(\d+)", HEADER.read_text()))
     for name, value in defines.items():
         key = {"MLAQ_NOPE_DIM": "NOPE_DIM", "MLAQ_NOPE_DIM_GLM": "NOPE_DIM_GLM", "MLAQ_LATENT_DIM": "LATENT_DIM",
-               "MLAQ_ROPE_DIM": "ROPE_DIM", "MLAQ_MAX_M": "MAX_M"}.get(name, name)
+               "MLAQ_ROPE_DIM": "ROPE_DIM", "MLAQ_MAX_M": "MAX_M", "MLAQ_V_DIM": "V_DIM"}.get(name, name)
         assert getattr(mq, key) == int(value), name
 
 
@@ -204,3 +205,50 @@ def test_run_ex_null_args_and_empty_batch(lib):
     assert lib.mlaq_run_ex(None, None) == INV
     assert "NULL" in mq.mlaq_last_error()
     assert run_ex(lib, M=0, q_nope=None, out=None, nope_dim=192) == OK
+
+
+
+@pytest.mark.parametrize("wf", [0, 1])
+@pytest.mark.parametrize("h", [8, 11, 16])
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_uv_gate_accepts(lib, wf, h, m):
+    assert mq.mlaq_uv_plan_supported(h, m, weight_format=wf) == OK
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    (dict(num_heads=12, max_m=1), UNS, "num_heads"),
+    (dict(num_heads=16, max_m=33), UNS, "max_m"),
+    (dict(num_heads=16, max_m=4, latent_dim=576), UNS, "dims"),
+    (dict(num_heads=16, max_m=4, v_dim=64), UNS, "dims"),
+    (dict(num_heads=16, max_m=4, arch="gfx942"), UNS, "not gfx950"),
+    (dict(num_heads=16, max_m=4, weight_format=5), INV, "weight_format"),
+    (dict(num_heads=16, max_m=4, arch=None), INV, "arch"),
+])
+def test_uv_gate_rejects(lib, args, status, msg):
+    assert mq.mlaq_uv_plan_supported(**args) == status
+    assert msg in mq.mlaq_last_error()
+
+
+def uv_run(lib, x=A, w=2 * A, s=None, out=4 * A, M=4, H=16, wf=0):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)
+    return lib.mlaq_uv_run(v(x), v(w), v(s), v(out), M, H, wf, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), INV, "non-NULL"),
+    (dict(out=None), INV, "non-NULL"),
+    (dict(wf=1), INV, "need w_uv_scales"),
+    (dict(s=8 * A), INV, "no w_uv_scales"),
+    (dict(x=A + 8), INV, "16-byte aligned"),
+    (dict(out=2 * A + 256), INV, "overlaps"),
+    (dict(H=7), UNS, "H=7"),
+    (dict(M=33), UNS, "M=33"),
+    (dict(wf=9), INV, "weight_format"),
+])
+def test_uv_run_rejects_before_any_device_call(lib, kw, status, msg):
+    assert uv_run(lib, **kw) == status
+    assert msg in mq.mlaq_last_error()
+
+
+def test_uv_empty_batch_is_a_noop(lib):
+    assert uv_run(lib, x=None, w=None, out=None, M=0) == OK
