@@ -48,6 +48,8 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "µs per fused MLA query call + achieved HBM GB/s, H=16, M=1..32, BF16/MXFP8"
 HBM_PEAK_GBS = 8000.0
+# Sources whose hash the recorded HBM-traffic figure belongs to.
+KERNEL_SOURCES = ("mlaq_kernels.hip", "mlaq_device.h", "mlaq_internal.h")
 H, M_STEP, LAYERS, COPIES = 16, 32, 64, 6
 
 
@@ -513,7 +515,7 @@ def measured_traffic():
         return None
     kv = dict(line.split(None, 1) for line in rec.read_text().splitlines() if line and not line.startswith("#"))
     csrc = ROOT / "mla_decode_query_amd" / "csrc"
-    h = hashlib.sha256((csrc / "mlaq_kernels.hip").read_bytes() + (csrc / "mlaq_internal.h").read_bytes())
+    h = hashlib.sha256(b"".join((csrc / f).read_bytes() for f in KERNEL_SOURCES))
     if h.hexdigest() != kv.get("kernel_source_sha256", "").strip():
         return None
     return int(kv["traffic_bytes_per_launch"])
