@@ -21,9 +21,18 @@ stated at the top of ``mlaq_oracle.c``:
   scale per 32 contiguous n of each k row (sparkinfer PR #75, review thread on
   ``api.py``: scale factors along n, N-major weight).
 
+* the V up-projection ``x[m,h,:] . W_UV[h,v,:]`` over the 512 latent values,
+  fp32 accumulation, bf16 output (vLLM PR #174, "Layout and topology
+  behavior" and "Safety scope and PR 173"; widths are readings);
+* dense MLA decode attention over a paged latent cache, evaluated directly or
+  through split partials stored as FP32 or BF16 and merged into a BF16 output
+  (b12x PR #441 "Allow FP32 split partials in prepared dense MLA", commit
+  text and "Behavior"), all in double.
+
 Parity pins: every function here is checked against values the mathematics
-fixes (tests/test_oracle_codecs.py, tests/test_oracle_pins.py); none is
-"parity unpinned".
+or an independent library fixes (tests/oracle_pins.py, run by
+tests/test_oracle_pins.py, and the planted mistakes of
+tests/test_oracle_mutants.py); none is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -42,6 +51,8 @@ LIB = _HERE / "libmlaq_oracle.so"
 WEIGHT_BF16, WEIGHT_MXFP8 = 0, 1
 OUT_BF16, OUT_E4M3 = 0, 1
 MX_BLOCK = 32
+PARTIAL_BF16, PARTIAL_FP32, PARTIAL_EXACT = 0, 1, 2
+SPLIT_ALIGN = 64
 
 GCC_FLAGS = ["-O2", "-std=gnu99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
 
@@ -78,10 +89,13 @@ def _declare(lib):
     lib.mlaq_oracle_run.argtypes = [P, P, P, P, ctypes.c_float, P] + [ctypes.c_int] * 7 + [P, P, P, ctypes.c_int]
     lib.mlaq_oracle_uv_run.restype = ctypes.c_int
     lib.mlaq_oracle_uv_run.argtypes = [P, P, P, P] + [ctypes.c_int] * 5 + [P, P]
+    lib.mlaq_oracle_attn_run.restype = ctypes.c_int
+    lib.mlaq_oracle_attn_run.argtypes = ([P, P, P, P] + [ctypes.c_int] * 7 + [ctypes.c_double]
+                                         + [ctypes.c_int] * 2 + [P] * 7 + [ctypes.c_int])
     lib.mlaq_oracle_qscale.restype = ctypes.c_float
     lib.mlaq_oracle_qscale.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t]
     for name in ("mlaq_oracle_bf16_round", "mlaq_oracle_e4m3_encode", "mlaq_oracle_e4m3_decode",
-                 "mlaq_oracle_e8m0_decode"):
+                 "mlaq_oracle_e8m0_decode", "mlaq_oracle_bf16_round_f64"):
         fn = getattr(lib, name)
         fn.restype = None
         fn.argtypes = [P, P, ctypes.c_size_t]
@@ -191,6 +205,58 @@ def uv_projection(x, w, w_scales=None, *, weight_format=WEIGHT_BF16, diagnostics
     return res
 
 
+def attention(q, kv, block_table, seq_lens, *, softmax_scale, num_splits=0, partial_dtype=PARTIAL_BF16,
+              dv=512, threads=8, diagnostics=True, lib_path=None):
+    """Dense MLA decode attention over a paged latent cache, on host arrays.
+
+    ``q`` uint16 (bf16) ``[M,H,D]``; ``kv`` uint16 ``[num_pages,P,D]`` (the
+    first ``dv`` entries of a row are the value); ``block_table`` int32
+    ``[M,max_blocks]``; ``seq_lens`` int32 ``[M]``. ``num_splits = 0``
+    evaluates the definition; ``num_splits >= 1`` runs the split procedure with
+    partials stored per ``partial_dtype``. The arithmetic is
+    ``mlaq_oracle_attn_run``.
+
+    Returns a dict: ``out`` (uint16 bf16 ``[M,H,dv]``) and, with
+    ``diagnostics``, ``o`` (fp64 merged output before rounding), ``lse``
+    (``[M,H]``), ``vabs`` (sum_t p_t |v_t|, ``[M,H,dv]``), ``smag`` (max_t of
+    scale * sum_d |q_d kv_t[d]|, ``[M,H]``) and, when split, ``part``
+    (``[M,S,H,dv]``) and ``plse`` (``[M,S,H]``): the stored partials.
+    """
+    lib = _load(lib_path)
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    block_table = _c(block_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    M, H, D = q.shape
+    num_pages, P, Dk = kv.shape
+    if Dk != D:
+        raise OracleError("cache rows must have the query's width")
+    if block_table.ndim != 2 or block_table.shape[0] != M or seq_lens.shape != (M,):
+        raise OracleError("block_table must be [M,max_blocks] and seq_lens [M]")
+    out = np.zeros((M, H, dv), np.uint16)
+    o = lse = vabs = smag = part = plse = None
+    if diagnostics:
+        o = np.zeros((M, H, dv), np.float64)
+        lse = np.zeros((M, H), np.float64)
+        vabs = np.zeros((M, H, dv), np.float64)
+        smag = np.zeros((M, H), np.float64)
+        if num_splits > 0:
+            part = np.zeros((M, num_splits, H, dv), np.float64)
+            plse = np.zeros((M, num_splits, H), np.float64)
+    rc = lib.mlaq_oracle_attn_run(_ptr(q), _ptr(kv), _ptr(block_table), _ptr(seq_lens), M, H, D, int(dv), P,
+                                  num_pages, block_table.shape[1], float(softmax_scale), int(num_splits),
+                                  int(partial_dtype), _ptr(out), _ptr(o), _ptr(lse), _ptr(vabs), _ptr(smag),
+                                  _ptr(part), _ptr(plse), int(threads))
+    if rc != 0:
+        raise OracleError(f"mlaq_oracle_attn_run failed with status {rc}")
+    res = {"out": out}
+    if diagnostics:
+        res.update(o=o, lse=lse, vabs=vabs, smag=smag)
+        if num_splits > 0:
+            res.update(part=part, plse=plse)
+    return res
+
+
 def qscale_from_result(acc, q_pe, lib_path=None) -> float:
     """amax/448 over the fp32 projection and q_pe (1.0 when amax is 0)."""
     lib = _load(lib_path)
@@ -210,6 +276,11 @@ def _elementwise(name, arr, in_dtype, out_dtype, lib_path=None):
 def bf16_round(x, lib_path=None):
     """fp32 array -> bf16 bit patterns (uint16), round to nearest even."""
     return _elementwise("mlaq_oracle_bf16_round", x, np.float32, np.uint16, lib_path)
+
+
+def bf16_round_f64(x, lib_path=None):
+    """float64 array -> bf16 bit patterns (uint16), one round to nearest even."""
+    return _elementwise("mlaq_oracle_bf16_round_f64", x, np.float64, np.uint16, lib_path)
 
 
 def e4m3_encode(x, lib_path=None):

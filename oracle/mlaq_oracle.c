@@ -1,6 +1,8 @@
 /*
  * mlaq_oracle.c -- plain, slow, CPU oracle for the fused MLA decode query
- * projection and assembly.
+ * projection and assembly, and for the two steps around it that the pages
+ * name: the V up-projection after attention and dense MLA decode attention
+ * with split partials (each in its own section below).
  *
  * TEST INFRASTRUCTURE ONLY. The product library never links, loads or calls
  * this file; only the test suite, the smoke check and the benchmark's
@@ -390,4 +392,318 @@ int mlaq_oracle_uv_run(const uint16_t* x, const void* w, const uint8_t* w_scales
   }
   free(wdq);
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense MLA decode attention with split partials (the query's consumer)    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Each of the M decode tokens m belongs to its own sequence, whose T_m =
+ * seq_lens[m] cached tokens live in a paged latent cache: token t of sequence
+ * m is row (t mod P) of physical page block_table[m][t / P], and a row holds
+ * the D = 576 values "512 latent, then 64 rotary" -- the same split as the
+ * query row. Attention runs in the latent space (keys are the whole row,
+ * values its first DV = 512 entries), per head h:
+ *
+ *   s_t  = softmax_scale * sum_{d<D} q[m,h,d] * kv_t[d]
+ *   o    = sum_{t<T} exp(s_t - L) kv_t[0:DV] / sum_{t<T} exp(s_t - L)
+ *   lse  = L + log sum_{t<T} exp(s_t - L),      L = max_t s_t
+ *
+ * Split procedure (b12x PR #441 "Allow FP32 split partials in prepared dense
+ * MLA": commit text, walkthrough and "Behavior"): the T tokens are cut into S
+ * contiguous ranges; range s yields its own normalized output o_s and lse_s;
+ * o_s is stored as FP32 or as BF16 (the default) and lse_s as fp32; a merge
+ * then forms
+ *
+ *   L' = max_s lse_s,  w_s = exp(lse_s - L'),
+ *   o  = sum_s w_s o_s / sum_s w_s,  lse = L' + log sum_s w_s,
+ *
+ * and the output is BF16 in every case. Readings where the page is silent
+ * (each is listed in the design notes):
+ *  - range boundaries: chunk = ceil(T / S) rounded up to a multiple of 64
+ *    tokens, range s = [s*chunk, min(T, (s+1)*chunk)); an empty range has
+ *    lse_s = -inf and takes no part in the merge;
+ *  - T = 0 gives o = 0 and lse = -inf;
+ *  - "stored as BF16/FP32" is round-to-nearest-even of the range's exact
+ *    normalized output; lse_s is stored as fp32 in both cases.
+ * Everything else is evaluated in double (bf16 inputs make each product
+ * exact; exp and log are the C library's).
+ */
+
+#define ORACLE_PARTIAL_BF16 0
+#define ORACLE_PARTIAL_FP32 1
+#define ORACLE_PARTIAL_EXACT 2 /* keep partials and lse_s in double (for checks) */
+#define ORACLE_SPLIT_ALIGN 64
+
+/* double -> bf16, round to nearest, ties to even, from the definition: bf16
+ * keeps 8 significant bits, so in the binade [2^(e-1), 2^e) its values are
+ * the multiples of 2^(e-8) (never finer than 2^-133, the subnormal spacing);
+ * take the two multiples that bracket |x|, keep the nearer, on a tie the even
+ * multiple. Results past the largest finite bf16 become infinity. */
+static uint16_t f64_to_bf16_rne(double x) {
+  if (isnan(x)) return (uint16_t)(signbit(x) ? 0xFFC0u : 0x7FC0u);
+  double a = fabs(x);
+  double r;
+  if (a == 0.0 || isinf(a)) {
+    r = a;
+  } else {
+    int e;
+    frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+    int se = e - 8;
+    if (se < -133) se = -133;
+    double step = ldexp(1.0, se);
+    double lo = floor(a / step); /* exact: a / step only shifts the exponent */
+    double dlo = a - lo * step, dhi = (lo + 1.0) * step - a;
+    if (dlo < dhi)
+      r = lo * step;
+    else if (dhi < dlo)
+      r = (lo + 1.0) * step;
+    else
+      r = fmod(lo, 2.0) == 0.0 ? lo * step : (lo + 1.0) * step;
+    if (r > 3.3895313892515355e38) r = INFINITY; /* past (2 - 2^-7) * 2^127 */
+  }
+  uint16_t b = (uint16_t)(bits_from_f32((float)r) >> 16); /* r is a bf16 value: exact */
+  return signbit(x) ? (uint16_t)(b | 0x8000u) : b;
+}
+
+typedef struct {
+  const uint16_t* q;           /* bf16 [M,H,D] */
+  const uint16_t* kv;          /* bf16 [num_pages,P,D] */
+  const int32_t* block_table;  /* [M, max_blocks] */
+  const int32_t* seq_lens;     /* [M] */
+  int M, H, D, DV, P, num_pages, max_blocks, num_splits, partial_dtype;
+  double softmax_scale;
+  uint16_t* out;      /* bf16 [M,H,DV] */
+  double* o_out;      /* optional [M,H,DV]: merged o before the bf16 rounding */
+  double* lse_out;    /* optional [M,H] */
+  double* vabs_out;   /* optional [M,H,DV]: sum_t p_t |kv_t[d]| with exact p */
+  double* smag_out;   /* optional [M,H]: max_t softmax_scale * sum_d |q_d kv_t[d]| */
+  double* part_out;   /* optional [M,S,H,DV]: stored partials (after rounding) */
+  double* plse_out;   /* optional [M,S,H]: stored lse_s (fp32 values) */
+  int next_item;      /* work counter over m, under the lock */
+  pthread_mutex_t lock;
+} attn_job;
+
+/* Pointer to the cached row of token t of sequence m. */
+static const uint16_t* attn_row(const attn_job* j, int m, int t) {
+  int page = j->block_table[(size_t)m * j->max_blocks + t / j->P];
+  return j->kv + ((size_t)page * j->P + (size_t)(t % j->P)) * j->D;
+}
+
+/* Softmax over tokens [a, b) of one (m, h): normalized output into o[DV],
+ * returns lse. Scores s[] are the precomputed s_t of the whole sequence. */
+static double attn_range(const attn_job* j, int m, const double* s, int a, int b, double* o) {
+  double L = -INFINITY, sum = 0.0;
+  for (int t = a; t < b; ++t)
+    if (s[t] > L) L = s[t];
+  for (int d = 0; d < j->DV; ++d) o[d] = 0.0;
+  for (int t = a; t < b; ++t) {
+    double e = exp(s[t] - L);
+    const uint16_t* row = attn_row(j, m, t);
+    sum += e;
+    for (int d = 0; d < j->DV; ++d) o[d] += e * (double)bf16_to_f32(row[d]);
+  }
+  for (int d = 0; d < j->DV; ++d) o[d] /= sum;
+  return L + log(sum);
+}
+
+static void attn_sequence(attn_job* j, int m, double* s, double* o, double* ps) {
+  const int H = j->H, D = j->D, DV = j->DV, T = j->seq_lens[m];
+  const int S = j->num_splits;
+  for (int h = 0; h < H; ++h) {
+    const uint16_t* qr = j->q + ((size_t)m * H + h) * D;
+    const size_t orow = ((size_t)m * H + h) * DV;
+    double smag = 0.0;
+    /* Step 1: scores s_t = scale * q . kv_t over all D dims. */
+    for (int t = 0; t < T; ++t) {
+      const uint16_t* row = attn_row(j, m, t);
+      double acc = 0.0, mag = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double p = (double)bf16_to_f32(qr[d]) * (double)bf16_to_f32(row[d]); /* exact */
+        acc += p;
+        mag += fabs(p);
+      }
+      s[t] = j->softmax_scale * acc;
+      if (j->softmax_scale * mag > smag) smag = j->softmax_scale * mag;
+    }
+    if (j->smag_out) j->smag_out[(size_t)m * H + h] = smag;
+    /* Bound helper: sum_t p_t |v_t| with the exact (unsplit) weights. */
+    if (j->vabs_out) {
+      double L = -INFINITY, sum = 0.0;
+      for (int t = 0; t < T; ++t)
+        if (s[t] > L) L = s[t];
+      for (int d = 0; d < DV; ++d) j->vabs_out[orow + d] = 0.0;
+      for (int t = 0; t < T; ++t) {
+        double e = exp(s[t] - L);
+        const uint16_t* row = attn_row(j, m, t);
+        sum += e;
+        for (int d = 0; d < DV; ++d) j->vabs_out[orow + d] += e * fabs((double)bf16_to_f32(row[d]));
+      }
+      for (int d = 0; d < DV; ++d) j->vabs_out[orow + d] = T > 0 ? j->vabs_out[orow + d] / sum : 0.0;
+    }
+    double lse;
+    if (T == 0) {
+      /* Step 2 for an empty sequence: nothing to attend to. */
+      for (int d = 0; d < DV; ++d) o[d] = 0.0;
+      lse = -INFINITY;
+      for (int sp = 0; sp < S; ++sp) {
+        if (j->plse_out) j->plse_out[((size_t)m * S + sp) * H + h] = -INFINITY;
+        if (j->part_out)
+          for (int d = 0; d < DV; ++d) j->part_out[(((size_t)m * S + sp) * H + h) * DV + d] = 0.0;
+      }
+    } else if (S == 0) {
+      /* Step 2 without splitting: the definition itself. */
+      lse = attn_range(j, m, s, 0, T, o);
+    } else {
+      /* Step 2: one normalized partial per range, stored in its dtype. */
+      int chunk = (T + S - 1) / S;
+      chunk = (chunk + ORACLE_SPLIT_ALIGN - 1) / ORACLE_SPLIT_ALIGN * ORACLE_SPLIT_ALIGN;
+      double Lp = -INFINITY;
+      double* plse = ps + (size_t)S * DV; /* S lse values after the S partial rows */
+      for (int sp = 0; sp < S; ++sp) {
+        double* po = ps + (size_t)sp * DV;
+        long a = (long)sp * chunk, b = a + chunk < T ? a + chunk : T;
+        if (a >= b) {
+          plse[sp] = -INFINITY;
+          for (int d = 0; d < DV; ++d) po[d] = 0.0;
+        } else {
+          plse[sp] = attn_range(j, m, s, (int)a, (int)b, po);
+          if (j->partial_dtype != ORACLE_PARTIAL_EXACT) plse[sp] = (double)(float)plse[sp];
+          for (int d = 0; d < DV; ++d) {
+            if (j->partial_dtype == ORACLE_PARTIAL_BF16)
+              po[d] = (double)bf16_to_f32(f64_to_bf16_rne(po[d]));
+            else if (j->partial_dtype == ORACLE_PARTIAL_FP32)
+              po[d] = (double)(float)po[d];
+          }
+        }
+        if (plse[sp] > Lp) Lp = plse[sp];
+        if (j->plse_out) j->plse_out[((size_t)m * S + sp) * H + h] = plse[sp];
+        if (j->part_out)
+          for (int d = 0; d < DV; ++d) j->part_out[(((size_t)m * S + sp) * H + h) * DV + d] = po[d];
+      }
+      /* Step 3: merge the ranges that hold tokens. */
+      double wsum = 0.0;
+      for (int d = 0; d < DV; ++d) o[d] = 0.0;
+      for (int sp = 0; sp < S; ++sp) {
+        if (plse[sp] == -INFINITY) continue;
+        double w = exp(plse[sp] - Lp);
+        wsum += w;
+        for (int d = 0; d < DV; ++d) o[d] += w * ps[(size_t)sp * DV + d];
+      }
+      for (int d = 0; d < DV; ++d) o[d] /= wsum;
+      lse = Lp + log(wsum);
+    }
+    /* Step 4: BF16 output. */
+    for (int d = 0; d < DV; ++d) {
+      j->out[orow + d] = f64_to_bf16_rne(o[d]);
+      if (j->o_out) j->o_out[orow + d] = o[d];
+    }
+    if (j->lse_out) j->lse_out[(size_t)m * H + h] = lse;
+  }
+}
+
+static void* attn_worker(void* arg) {
+  attn_job* j = (attn_job*)arg;
+  int tmax = 0;
+  for (int m = 0; m < j->M; ++m)
+    if (j->seq_lens[m] > tmax) tmax = j->seq_lens[m];
+  double* s = (double*)malloc(sizeof(double) * (size_t)(tmax > 0 ? tmax : 1));
+  double* o = (double*)malloc(sizeof(double) * (size_t)j->DV);
+  double* ps = (double*)malloc(sizeof(double) * ((size_t)j->num_splits * (j->DV + 1) + 1));
+  if (s && o && ps)
+    for (;;) {
+      pthread_mutex_lock(&j->lock);
+      int m = j->next_item++;
+      pthread_mutex_unlock(&j->lock);
+      if (m >= j->M) break;
+      attn_sequence(j, m, s, o, ps);
+    }
+  int failed = !(s && o && ps);
+  free(s);
+  free(o);
+  free(ps);
+  return failed ? (void*)1 : NULL;
+}
+
+/*
+ * Dense MLA decode attention over a paged latent cache. num_splits = 0
+ * evaluates the definition directly; num_splits >= 1 runs the split procedure
+ * with partials stored per partial_dtype (0 BF16, 1 FP32, 2 kept in double).
+ * Returns 0, or 1 on bad sizes or modes, 2 on missing buffers, 3 on host
+ * allocation failure, 4 on a block-table entry or sequence length outside the
+ * cache. Sequences are independent and split over `nthreads` threads; results
+ * do not depend on the thread count.
+ */
+int mlaq_oracle_attn_run(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
+                         const int32_t* seq_lens, int M, int H, int D, int DV, int P, int num_pages,
+                         int max_blocks, double softmax_scale, int num_splits, int partial_dtype,
+                         uint16_t* out, double* o_out, double* lse_out, double* vabs_out, double* smag_out,
+                         double* part_out, double* plse_out, int nthreads) {
+  attn_job j;
+  if (M < 0 || H < 0 || D < 1 || DV < 1 || DV > D || P < 1 || num_pages < 0 || max_blocks < 0) return 1;
+  if (num_splits < 0 || partial_dtype < ORACLE_PARTIAL_BF16 || partial_dtype > ORACLE_PARTIAL_EXACT) return 1;
+  if (M == 0 || H == 0) return 0;
+  if (!q || !seq_lens || !out) return 2;
+  for (int m = 0; m < M; ++m) {
+    long T = seq_lens[m];
+    if (T < 0 || T > (long)max_blocks * P) return 4;
+    if (T > 0 && (!kv || !block_table)) return 2;
+    for (long b = 0; b < (T + P - 1) / P; ++b) {
+      int page = block_table[(size_t)m * max_blocks + b];
+      if (page < 0 || page >= num_pages) return 4;
+    }
+  }
+  memset(&j, 0, sizeof j);
+  j.q = q;
+  j.kv = kv;
+  j.block_table = block_table;
+  j.seq_lens = seq_lens;
+  j.M = M;
+  j.H = H;
+  j.D = D;
+  j.DV = DV;
+  j.P = P;
+  j.num_pages = num_pages;
+  j.max_blocks = max_blocks;
+  j.num_splits = num_splits;
+  j.partial_dtype = partial_dtype;
+  j.softmax_scale = softmax_scale;
+  j.out = out;
+  j.o_out = o_out;
+  j.lse_out = lse_out;
+  j.vabs_out = vabs_out;
+  j.smag_out = smag_out;
+  j.part_out = num_splits > 0 ? part_out : NULL;
+  j.plse_out = num_splits > 0 ? plse_out : NULL;
+  pthread_mutex_init(&j.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > M) nthreads = M;
+  int status = 0;
+  if (nthreads == 1) {
+    if (attn_worker(&j)) status = 3;
+  } else {
+    pthread_t* tids = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int started = 0;
+    if (!tids) {
+      pthread_mutex_destroy(&j.lock);
+      return 3;
+    }
+    for (int t = 0; t < nthreads; ++t)
+      if (pthread_create(&tids[t], NULL, attn_worker, &j) == 0) ++started;
+    if (started == 0 && attn_worker(&j)) status = 3;
+    for (int t = 0; t < started; ++t) {
+      void* r = NULL;
+      pthread_join(tids[t], &r);
+      if (r) status = 3;
+    }
+    free(tids);
+  }
+  pthread_mutex_destroy(&j.lock);
+  return status;
+}
+
+/* Element-wise entry point of the double -> bf16 rounding, for pinning it. */
+void mlaq_oracle_bf16_round_f64(const double* in, uint16_t* out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = f64_to_bf16_rne(in[i]);
 }

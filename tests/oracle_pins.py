@@ -446,3 +446,195 @@ def check_uv_brute_force(lib=None):
 
 
 ALL_CHECKS.extend([check_uv_identity, check_uv_scale_closed_form, check_uv_brute_force])
+
+
+# --------------------------------------------------------------------------
+# Dense MLA decode attention with split partials
+# --------------------------------------------------------------------------
+
+def check_bf16_round_f64(lib=None):
+    """double -> bf16 against an independent route: round to odd into fp32
+    (truncate toward zero, set the last bit when inexact), then torch's fp32 ->
+    bf16 cast. With 16 extra bits, round-to-odd followed by round-to-nearest
+    gives the correctly rounded result (Boldo and Melquiond, "Emulation of FMA
+    and correctly rounded sums: proved algorithms using rounding to odd").
+    Midpoints and their double-precision neighbours, where a plain double ->
+    fp32 -> bf16 route would round twice, are included."""
+    rng = _rng(31)
+    mags = np.ldexp(rng.random(20000) + 0.5, rng.integers(-140, 128, 20000))
+    x = np.concatenate([mags * rng.choice([-1.0, 1.0], 20000), [0.0, -0.0, 1.0, -2.5]])
+    # exact midpoints between neighbouring bf16 values and one double ulp either side
+    lo = _f32(np.arange(0x3F80, 0x3FC0, dtype=np.uint16)).astype(np.float64)
+    hi = _f32(np.arange(0x3F81, 0x3FC1, dtype=np.uint16)).astype(np.float64)
+    mid = (lo + hi) / 2
+    x = np.concatenate([x, mid, np.nextafter(mid, 0.0), np.nextafter(mid, 4.0), -mid,
+                        [3.3895313892515355e38, 3.3961775292304957e38, 3.4e38, 1e300, 2.0 ** -133, 2.0 ** -134,
+                         3 * 2.0 ** -135, 2.0 ** -140]])
+    ours = oracle.bf16_round_f64(x, lib_path=lib)
+    with np.errstate(over="ignore"):
+        f = x.astype(np.float32)  # round to nearest
+    f64 = f.astype(np.float64)
+    over = np.abs(f64) > np.abs(x)
+    f = np.where(over, np.nextafter(f, np.float32(0)), f)  # toward zero
+    inexact = f.astype(np.float64) != x
+    fb = f.view(np.uint32) | inexact.astype(np.uint32)  # round to odd
+    fb = np.where(np.isinf(f), f.view(np.uint32), fb)
+    ref = torch.from_numpy(fb.view(np.float32).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    big = np.abs(x) >= 3.3961775292304957e38  # past the last midpoint: infinity
+    ref = np.where(big, np.where(x > 0, 0x7F80, 0xFF80), ref).astype(np.uint16)
+    bad = ours != ref
+    assert not bad.any(), f"double -> bf16 differs at {x[bad][:4]}: {ours[bad][:4]} vs {ref[bad][:4]}"
+
+
+def _attn(inp, lib=None, **kw):
+    return oracle.attention(inp.q, inp.kv, inp.block_table, inp.seq_lens,
+                            softmax_scale=inp.softmax_scale, lib_path=lib, **kw)
+
+
+def _gather(inp, m):
+    """Rows of sequence m in token order, by numpy indexing (float64)."""
+    T = int(inp.seq_lens[m])
+    t = np.arange(T)
+    pages = inp.block_table[m, t // inp.page_size]
+    rows = inp.kv[pages, t % inp.page_size]
+    return _f32(rows).astype(np.float64)
+
+
+def _attn_case(seed, H, lens, P=64, **kw):
+    from workloads import make_attn_inputs
+
+    return make_attn_inputs(seed, H, lens, page_size=P, **kw)
+
+
+def check_attn_against_sdpa(lib=None):
+    """The unsplit definition against torch's scaled_dot_product_attention in
+    float64 on the CPU (keys = whole 576-wide row, values = its first 512
+    entries, shared by all heads), and lse against torch.logsumexp of the
+    scores. Covers several pages per sequence, page size 16 and 64, and scores
+    large enough that exp without the max shift would overflow."""
+    for P, lens, qstd in ((64, [1, 70, 200, 129], 1.0), (16, [33, 5, 64], 1.0), (64, [90, 3], 40.0)):
+        inp = _attn_case(1100 + P + len(lens), 5, lens, P=P, q_std=qstd)
+        res = _attn(inp, lib)
+        for m in range(inp.M):
+            rows = _gather(inp, m)
+            q = torch.from_numpy(_f32(inp.q[m]).astype(np.float64))  # [H,576]
+            k = torch.from_numpy(rows)  # [T,576]
+            v = torch.from_numpy(rows[:, :512].copy())
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None, :, None, :], k[None, None].expand(1, inp.H, -1, -1),
+                v[None, None].expand(1, inp.H, -1, -1), scale=inp.softmax_scale)[0, :, 0, :].numpy()
+            got = res["o"][m]
+            err = np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300)
+            assert err < 1e-11, f"P={P} m={m}: o differs from SDPA by {err}"
+            lse_ref = torch.logsumexp(inp.softmax_scale * (q @ k.T), dim=1).numpy()
+            assert np.allclose(res["lse"][m], lse_ref, rtol=1e-12, atol=1e-9), f"P={P} m={m}: lse"
+
+
+def check_attn_closed_forms(lib=None):
+    """q = 0: o is the plain mean of the values. T = 1: the value row itself,
+    bit for bit. Two tokens: logistic weights. T = 0: o = 0, lse = -inf."""
+    inp = _attn_case(1200, 3, [130, 1, 0])
+    inp.q[0] = 0
+    res = _attn(inp, lib)
+    mean = _gather(inp, 0)[:, :512].mean(axis=0)
+    assert np.allclose(res["o"][0], mean[None, :], rtol=1e-13, atol=1e-15), "q = 0 must average the values"
+    t0 = inp.block_table[1, 0]
+    assert np.array_equal(res["out"][1], np.broadcast_to(inp.kv[t0, 0, :512], (3, 512))), "T = 1 must copy"
+    assert np.all(res["out"][2] == 0) and np.all(np.isneginf(res["lse"][2])), "T = 0"
+    # two tokens, q one-hot at rotary dim 530: weights 1/(1 + e^-d), d = scale*a*(x1 - x0)
+    two = _attn_case(1201, 2, [2])
+    a, x0, x1 = 3.0, 0.5, -1.25
+    two.q[:] = 0
+    two.q[0, :, 530] = bf16_bits(np.array([a, 2 * a], np.float32))
+    pg = two.block_table[0, 0]
+    two.kv[pg, 0, 530], two.kv[pg, 1, 530] = bf16_bits(np.array([x0, x1], np.float32))
+    res = _attn(two, lib)
+    v = _gather(two, 0)[:, :512]
+    for h, ah in enumerate((a, 2 * a)):
+        d = two.softmax_scale * ah * (x1 - x0)
+        w1 = 1.0 / (1.0 + np.exp(-d))
+        assert np.allclose(res["o"][0, h], (1 - w1) * v[0] + w1 * v[1], rtol=1e-13, atol=1e-15), "two tokens"
+
+
+def check_attn_splits(lib=None):
+    """Merging exact split partials reproduces the unsplit result (the
+    log-sum-exp identity) for any split count; the stored partials and their
+    lse match an independent numpy evaluation of each 64-aligned range; FP32
+    partials stay within fp32 rounding of the exact result; BF16 partials are
+    the bf16 rounding of the exact partial, so one split gives the unsplit
+    output bit for bit, and several move the result by at most a bf16 step."""
+    inp = _attn_case(1300, 4, [200, 64, 1000, 65, 7])
+    exact = _attn(inp, lib)
+    for S in (1, 2, 3, 5, 64):
+        r = _attn(inp, lib, num_splits=S, partial_dtype=oracle.PARTIAL_EXACT)
+        assert np.allclose(r["o"], exact["o"], rtol=1e-12, atol=1e-14), f"S={S}: merge identity"
+        assert np.allclose(r["lse"], exact["lse"], rtol=1e-12, atol=1e-12), f"S={S}: merged lse"
+    # range boundaries: T = 200, S = 3 -> chunk 67 rounded up to 128: [0,128), [128,200), empty
+    S = 3
+    r = _attn(inp, lib, num_splits=S, partial_dtype=oracle.PARTIAL_EXACT)
+    rows = _gather(inp, 0)
+    q = _f32(inp.q[0]).astype(np.float64)
+    sc = inp.softmax_scale * (q @ rows.T)  # [H,T]
+    for s, (a, b) in enumerate(((0, 128), (128, 200))):
+        seg = sc[:, a:b]
+        mx = seg.max(axis=1, keepdims=True)
+        e = np.exp(seg - mx)
+        lse = mx[:, 0] + np.log(e.sum(axis=1))
+        part = (e @ rows[a:b, :512]) / e.sum(axis=1, keepdims=True)
+        assert np.allclose(r["plse"][0, s], lse, rtol=1e-12, atol=1e-12), f"range {s}: lse_s"
+        assert np.allclose(r["part"][0, s], part, rtol=1e-12, atol=1e-14), f"range {s}: partial"
+    assert np.all(np.isneginf(r["plse"][0, 2])), "third range of T=200, S=3 is empty"
+    # storage dtypes
+    f32 = _attn(inp, lib, num_splits=5, partial_dtype=oracle.PARTIAL_FP32)
+    scale = np.max(np.abs(exact["o"]))
+    assert np.max(np.abs(f32["o"] - exact["o"])) <= 64 * 2.0 ** -24 * scale, "FP32 partials"
+    assert np.array_equal(f32["part"], f32["part"].astype(np.float32).astype(np.float64)), "FP32 storage"
+    ex5 = _attn(inp, lib, num_splits=5, partial_dtype=oracle.PARTIAL_EXACT)
+    want_lse = ex5["plse"].astype(np.float32).astype(np.float64)
+    assert np.array_equal(f32["plse"], want_lse), "lse_s is stored as the nearest fp32"
+    b16 = _attn(inp, lib, num_splits=5, partial_dtype=oracle.PARTIAL_BF16)
+    assert np.array_equal(b16["plse"], want_lse), "lse_s is fp32 with BF16 partials too"
+    live = np.isfinite(ex5["plse"])[..., None] & np.ones_like(ex5["part"], bool)
+    want = torch.from_numpy(ex5["part"][live].astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    close = np.abs(b16["part"][live] - ex5["part"][live]) <= _ulp_bf16(ex5["part"][live]) / 2 * (1 + 1e-9)
+    assert close.all(), "BF16 partials must be the nearest bf16 of the exact partial"
+    assert np.mean(b16["part"][live] == want) > 0.99, "BF16 partials"
+    assert np.max(np.abs(b16["o"] - exact["o"])) <= 2.0 ** -8 * scale, "BF16 partials move o by < 1 step"
+    assert np.max(np.abs(b16["o"] - exact["o"])) > 0, "BF16 partials must round"
+    one = _attn(inp, lib, num_splits=1, partial_dtype=oracle.PARTIAL_BF16)
+    assert np.array_equal(one["out"], exact["out"]), "one BF16 split = the unsplit bf16 output"
+
+
+def check_attn_invariants(lib=None):
+    """Moving a sequence's pages elsewhere in the pool, or changing the thread
+    count, changes no output bit; each sequence and head is computed on its own
+    (a batch gives the same bits as the sequences alone)."""
+    inp = _attn_case(1400, 6, [300, 17, 128])
+    base = _attn(inp, lib, num_splits=3)
+    moved = _attn_case(1400, 6, [300, 17, 128])
+    n = moved.kv.shape[0]
+    perm = _rng(5).permutation(n)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(n)
+    moved.kv = moved.kv[perm]
+    moved.block_table = np.where(moved.block_table >= 0, inv[np.maximum(moved.block_table, 0)], -1).astype(np.int32)
+    for kw in ({"num_splits": 3}, {"num_splits": 3, "threads": 1}):
+        r = _attn(moved, lib, **kw)
+        assert np.array_equal(r["out"], base["out"]) and np.array_equal(r["lse"], base["lse"]), f"pages moved {kw}"
+    for m in range(inp.M):
+        one = _attn_case(1400, 6, [300, 17, 128])
+        one.q, one.block_table, one.seq_lens = one.q[m:m + 1], one.block_table[m:m + 1], one.seq_lens[m:m + 1]
+        r = _attn(one, lib, num_splits=3)
+        assert np.array_equal(r["out"][0], base["out"][m]), f"sequence {m} alone"
+        r = _attn(dataclass_replace(one, q=one.q[:, 2:4].copy()), lib, num_splits=3)
+        assert np.array_equal(r["out"][0], base["out"][m, 2:4]), f"heads 2..3 of sequence {m}"
+
+
+def dataclass_replace(obj, **kw):
+    import dataclasses
+
+    return dataclasses.replace(obj, **kw)
+
+
+ALL_CHECKS.extend([check_bf16_round_f64, check_attn_against_sdpa, check_attn_closed_forms, check_attn_splits,
+                   check_attn_invariants])

@@ -31,6 +31,20 @@ MUTANTS = {
     "uv_weight_as_HCV": ("size_t idx = ((size_t)h * V + v) * C + c;", "size_t idx = ((size_t)h * C + c) * V + v;"),
     "uv_drop_last_c": ("for (int c = 0; c < C; ++c) {\n          double p", "for (int c = 0; c < C - 1; ++c) {\n          double p"),
     "projection_offset_by_one": ("((uint16_t*)j->out)[orow + n] = y;", "((uint16_t*)j->out)[orow + (n + 1) % N] = y;"),
+    "attn_scale_missing": ("s[t] = j->softmax_scale * acc;", "s[t] = acc;"),
+    "attn_value_from_rope": ("o[d] += e * (double)bf16_to_f32(row[d]);",
+                             "o[d] += e * (double)bf16_to_f32(row[d + (j->D - j->DV)]);"),
+    "attn_drop_last_token": ("for (int t = a; t < b; ++t) {\n    double e", "for (int t = a; t < b - 1; ++t) {\n    double e"),
+    "attn_row_off_by_one": ("(size_t)(t % j->P)) * j->D;", "(size_t)((t + 1) % j->P)) * j->D;"),
+    "attn_split_align_32": ("#define ORACLE_SPLIT_ALIGN 64", "#define ORACLE_SPLIT_ALIGN 32"),
+    "attn_merge_weight_inverted": ("double w = exp(plse[sp] - Lp);", "double w = exp(Lp - plse[sp]);"),
+    "attn_bf16_partial_skipped": ("po[d] = (double)bf16_to_f32(f64_to_bf16_rne(po[d]));", "po[d] = (double)(float)po[d];"),
+    "attn_lse_kept_double": ("if (j->partial_dtype != ORACLE_PARTIAL_EXACT) plse[sp] = (double)(float)plse[sp];", "(void)0;"),
+    "attn_no_max_shift": ("double e = exp(s[t] - L);\n    const uint16_t* row", "double e = exp(s[t]);\n    const uint16_t* row"),
+    "attn_lse_without_max": ("return L + log(sum);", "return log(sum);"),
+    "attn_last_range_short": ("b = a + chunk < T ? a + chunk : T;", "b = a + chunk < T ? a + chunk : T - 1;"),
+    "f64_bf16_ties_up": ("r = fmod(lo, 2.0) == 0.0 ? lo * step : (lo + 1.0) * step;", "r = (lo + 1.0) * step;"),
+    "f64_bf16_one_bit_short": ("int se = e - 8;", "int se = e - 7;"),
 }
 
 

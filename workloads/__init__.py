@@ -23,6 +23,18 @@ Recipe (all draws from ``numpy.random.Generator(PCG64(seed))`` in this order):
   3. q_pe    ~ N(0, 1), fp32, then bf16                       [M_draw, H, R]
 The M sweep draws at ``M_draw`` (default 32) and a call with M tokens uses
 the first M rows, so one seed serves every M of a sweep.
+
+Dense MLA decode attention (``make_attn_inputs``): M sequences with one query
+each and ragged cached lengths, a paged latent cache of 576-wide rows (512
+latent, then 64 rotary) and a block table that scatters each sequence's pages
+over the pool in random order (so page indices run high and out of order; the
+vLLM page's serving check covers high cache-page indices). Recipe, in order:
+  1. q   ~ N(0, q_std), fp32, then bf16                       [M, H, 576]
+  2. kv  ~ N(0, kv_std), fp32, then bf16                      [num_pages, P, 576]
+  3. a permutation of the num_pages physical pages; sequence m takes the next
+     ceil(T_m / P) of them in order; unused table entries are -1.
+softmax_scale defaults to 1/sqrt(192) (128 nope + 64 rope dims per head). The
+pages' serving runs (4096-token outputs, 64k contexts) stand in as lengths.
 """
 
 from __future__ import annotations
@@ -116,3 +128,73 @@ def algorithmic_bytes(M: int, H: int, weight_format: int, out_dtype: int, K: int
     sb = H * K * (N // MX_BLOCK) if weight_format == WEIGHT_MXFP8 else 0
     ob = M * H * (N + R) * (2 if out_dtype == OUT_BF16 else 1)
     return wb + sb + M * H * K * 2 + M * H * R * 2 + ob + (4 if out_dtype == OUT_E4M3 else 0)
+
+
+D_ROW = N_LATENT + R_ROPE
+ATTN_PAGE = 64
+PARTIAL_BF16, PARTIAL_FP32 = 0, 1
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    """Host bit patterns of one decode-attention batch."""
+
+    q: np.ndarray  # uint16 [M,H,576]
+    kv: np.ndarray  # uint16 [num_pages,P,576]
+    block_table: np.ndarray  # int32 [M,max_blocks], -1 where unused
+    seq_lens: np.ndarray  # int32 [M]
+    softmax_scale: float
+    seed: int
+
+    @property
+    def M(self):
+        return self.q.shape[0]
+
+    @property
+    def H(self):
+        return self.q.shape[1]
+
+    @property
+    def page_size(self):
+        return self.kv.shape[1]
+
+
+def make_attn_inputs(seed: int, H: int, seq_lens, page_size: int = ATTN_PAGE, spare_pages: int = 2,
+                     max_blocks: int | None = None, q_std: float = 1.0, kv_std: float = 1.0,
+                     softmax_scale: float = 192.0 ** -0.5) -> AttnInputs:
+    """Draw one seeded decode-attention batch (recipe in the module docstring)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(seq_lens, np.int64)
+    M = lens.shape[0]
+    blocks = (lens + page_size - 1) // page_size
+    total = int(blocks.sum())
+    num_pages = total + spare_pages
+    if max_blocks is None:
+        max_blocks = max(int(blocks.max()) if M else 0, 1)
+    q = _bf16_bits(rng.standard_normal((M, H, D_ROW), dtype=np.float32) * np.float32(q_std))
+    kv = np.empty((num_pages, page_size, D_ROW), np.uint16)
+    step = max(1, (1 << 24) // (page_size * D_ROW))  # draw in slabs of about 16M values
+    for p0 in range(0, num_pages, step):
+        p1 = min(num_pages, p0 + step)
+        kv[p0:p1] = _bf16_bits(rng.standard_normal((p1 - p0, page_size, D_ROW), dtype=np.float32)
+                               * np.float32(kv_std))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((M, max_blocks), -1, np.int32)
+    nxt = 0
+    for m in range(M):
+        b = int(blocks[m])
+        table[m, :b] = perm[nxt:nxt + b]
+        nxt += b
+    return AttnInputs(q=q, kv=kv, block_table=table, seq_lens=lens.astype(np.int32),
+                      softmax_scale=float(softmax_scale), seed=seed)
+
+
+def attn_algorithmic_bytes(seq_lens, H: int, page_size: int = ATTN_PAGE) -> int:
+    """Bytes one attention call must move, each counted once: every cached row
+    of every sequence (576 bf16), the queries, the block-table entries in use,
+    the sequence lengths and the bf16 [M,H,512] output. Split partials are
+    the implementation's own traffic and are not counted."""
+    lens = np.asarray(seq_lens, np.int64)
+    M = lens.shape[0]
+    blocks = int(((lens + page_size - 1) // page_size).sum())
+    return int(lens.sum()) * D_ROW * 2 + M * H * D_ROW * 2 + blocks * 4 + M * 4 + M * H * N_LATENT * 2
