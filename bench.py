@@ -26,6 +26,9 @@ Printed JSON line (stdout, one line):
               cold) fused vs staged per layer, and their AB/BA graph-replay
               comparison over H=8/11/16 x M=1/4/32
   uv_projection the V up-projection that follows attention, same step form
+  attention   dense MLA decode attention with BF16 / FP32 split partials over
+              a cold paged cache: 32 x 4096 tokens and 1 x 65536 tokens,
+              H=16, us per call and GB/s against the HBM peak
   staged      the staged path (torch.bmm + copies + E4M3 quantization) of the
               same step on the same GPU
   cpu_baseline the CPU oracle timed on this host over a bounded sample of the
@@ -66,6 +69,7 @@ def parse():
     p.add_argument("--no-per-call", action="store_true")
     p.add_argument("--no-pages-shape", action="store_true")
     p.add_argument("--no-uv", action="store_true")
+    p.add_argument("--no-attention", action="store_true")
     p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -469,6 +473,59 @@ def uv_leg(torch, mq, wl, args):
             "bytes_per_step": nbytes}
 
 
+def attention_leg(torch, mq, wl, args):
+    """Dense MLA decode attention with split partials over a paged latent
+    cache (page 64, bf16 rows of 576), the library's split count, BF16 and
+    FP32 partials. Two shapes: a decode batch of 32 sequences x 4096 cached
+    tokens and one 65,536-token sequence, 16 heads. Several copies of the
+    cache (over 600 MB in all, past the 256 MB Infinity Cache) are read in
+    turn inside one hipGraph, so every call streams its cache from HBM.
+    Inputs: workloads.make_attn_inputs (seed 9000 + shape index)."""
+    shapes = [("decode batch: 32 sequences x 4096 cached tokens", 32, 4096, 4),
+              ("64k context: 1 sequence x 65536 cached tokens", 1, 65536, 8)]
+    res = []
+    stream = torch.cuda.Stream()
+    for idx, (name, M, T, copies) in enumerate(shapes):
+        inp = wl.make_attn_inputs(9000 + idx, H, [T] * M)
+        q = dev_bf16(torch, inp.q)
+        bt = torch.from_numpy(inp.block_table).cuda()
+        sl = torch.from_numpy(inp.seq_lens).cuda()
+        kv_host = torch.from_numpy(inp.kv.view(np.int16)).view(torch.bfloat16)
+        pools = [kv_host.cuda() for _ in range(copies)]
+        del kv_host
+        S = mq.mlaq_attn_num_splits(M, T)
+        nbytes = wl.attn_algorithmic_bytes(inp.seq_lens, H)
+        row = {"workload": name, "heads": H, "sequences": M, "tokens_per_sequence": T, "page_size": 64,
+               "num_splits": S, "bytes_per_call": nbytes, "cache_copies": copies}
+        for pd, tag in ((mq.MLAQ_PARTIAL_BF16, "bf16_partials"), (mq.MLAQ_PARTIAL_FP32, "fp32_partials")):
+            mq.mlaq_attn_prewarm(pd)
+            out = torch.empty((M, H, 512), dtype=torch.bfloat16, device="cuda")
+            n = mq.mlaq_attn_workspace_size(M, H, S, pd)
+            ws = torch.empty((n,), dtype=torch.uint8, device="cuda") if n else None
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                    for kv in pools:
+                        mq.mlaq_attn_run(q, kv, bt, sl, out, inp.softmax_scale, S, pd, ws)
+            torch.cuda.synchronize()
+            us = time_graphs(torch, [g], max(4, args.steps // 2), max(2, args.warmup // 2),
+                             per_step_units=copies) * 1e3
+            gbs = nbytes / (us * 1e-6) / 1e9
+            row[tag] = {"us_per_call": round(us, 3), "gbs": round(gbs, 1),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                        "workspace_bytes": n}
+            log(f"[bench] attention {name}, {tag}, S={S}: {us:.2f} us/call, {gbs:.1f} GB/s "
+                f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+            del g, ws, out
+        del pools
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res.append(row)
+    return res
+
+
 def cpu_baseline_leg(wl, layers, budget_s):
     """The CPU oracle on the step's layers, cycling through them until the
     time budget is spent (the oracle as it stands, threaded over heads)."""
@@ -557,6 +614,7 @@ def main():
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
     pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
     uv = None if args.no_uv else uv_leg(torch, mq, wl, args)
+    attn = None if args.no_attention else attention_leg(torch, mq, wl, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
@@ -591,6 +649,7 @@ def main():
         "per_call": per_call,
         "pages_shape": pages,
         "uv_projection": uv,
+        "attention": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -31,6 +31,7 @@
 #ifndef MLAQ_H_
 #define MLAQ_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -186,6 +187,83 @@ int mlaq_uv_can_implement(int num_heads, int max_m, int latent_dim, int v_dim, i
 int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_format, int device);
 int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
                 int weight_format, void* stream);
+
+/*
+ * Dense MLA decode attention with split partials, the consumer of the
+ * 576-wide query row (b12x PR #441 "Allow FP32 split partials in prepared
+ * dense MLA": commit text, walkthrough, "Behavior"). For each decode token m
+ * (one sequence with T_m = seq_lens[m] cached tokens) and head h < H:
+ *
+ *   s_t  = softmax_scale * q[m,h,0:576] . kv_t[0:576]      t < T_m
+ *   out[m,h,:] = bf16_rne( sum_t softmax(s)_t kv_t[0:512] )
+ *   lse[m,h]   = log sum_t exp(s_t)                         (natural log)
+ *
+ * Token t of sequence m is row (t mod page_size) of physical page
+ * block_table[m * block_table_stride + t / page_size] of the paged cache;
+ * a row is 512 latent values then 64 rotary values (bf16), the key is the
+ * whole row and the value its latent part, shared by all heads.
+ *
+ * The tokens are cut into num_splits ranges of ceil(T/S) rounded up to 64
+ * tokens; each range stores its normalized output (MLAQ_PARTIAL_BF16, the
+ * default, or MLAQ_PARTIAL_FP32, which avoids the intermediate rounding and
+ * doubles the partial bytes) and its lse in fp32 in the caller's workspace,
+ * and a merge kernel forms the BF16 output. With num_splits = 1 the single
+ * range is written straight to `out` (identical result, no merge launch).
+ * T_m = 0 gives out = 0 and lse = -inf.
+ *
+ *   q             bf16 [M,H,576] at q + m*q_stride_m + h*q_stride_h (elements,
+ *                 multiples of 8), rows contiguous, 16-byte aligned
+ *   kv_cache      bf16 [num_pages, page_size, 576], contiguous, 16-byte aligned
+ *   block_table   int32 [M, block_table_stride], 4-byte aligned
+ *   seq_lens      int32 [M], 4-byte aligned
+ *   out           bf16 [M,H,512], contiguous, 16-byte aligned
+ *   lse           fp32 [M,H] or NULL
+ *   workspace     mlaq_attn_workspace_size(M, H, num_splits, partial_dtype)
+ *                 bytes, 256-byte aligned (NULL allowed when that size is 0);
+ *                 scratch owned by the caller, overwritten by every call
+ *
+ * Device-side values are never trusted: seq_lens[m] is clamped into
+ * [0, block_table_stride * page_size] and every block-table entry that is
+ * read into [0, num_pages); only the entries of blocks below the clamped
+ * length are read. Limits (else MLAQ_ERR_UNSUPPORTED): 1 <= H <= 16,
+ * 1 <= page_size <= 4096, 1 <= num_splits <= 256, M <= 65536,
+ * block_table_stride * page_size <= 2^30 tokens. M = 0 is a
+ * no-op. Same status codes, asynchrony, graph-capturability and determinism
+ * as mlaq_run; out, lse and workspace must not overlap the inputs or each
+ * other.
+ */
+#define MLAQ_PARTIAL_BF16 0
+#define MLAQ_PARTIAL_FP32 1
+#define MLAQ_ATTN_ROW 576
+#define MLAQ_ATTN_MAX_HEADS 16
+#define MLAQ_ATTN_MAX_SPLITS 256
+#define MLAQ_ATTN_SPLIT_ALIGN 64
+
+typedef struct mlaq_attn_args {
+  const void* q;
+  int64_t q_stride_m, q_stride_h;
+  const void* kv_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  float softmax_scale;
+  int M, H, page_size, num_pages, block_table_stride, num_splits, partial_dtype;
+} mlaq_attn_args;
+
+/* Workspace bytes for a plan (0 when num_splits = 1, or for an invalid plan). */
+size_t mlaq_attn_workspace_size(int M, int H, int num_splits, int partial_dtype);
+/* Split count that fills `device` for M sequences of at most max_seq_len
+ * tokens (M * num_splits at most one workgroup per compute unit, ranges of
+ * at least 256 tokens, at least 1); written to *num_splits. */
+int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits);
+int mlaq_attn_plan_supported(int num_heads, int page_size, int num_splits, int partial_dtype, const char* arch);
+int mlaq_attn_can_implement(int num_heads, int page_size, int num_splits, int partial_dtype, int device);
+/* Loads both kernels of a partial dtype (and the one-split kernel). */
+int mlaq_attn_prewarm(int partial_dtype, int device);
+int mlaq_attn_run(const mlaq_attn_args* args, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the thread's next mlaq_* call. */

@@ -20,7 +20,11 @@ The entry points carry the C names (see ``include/mlaq.h``):
   a pitched output workspace) and nope width 128 or 192;
 * ``mlaq_uv_*``           -- the V up-projection that follows attention:
   ``out[m,h,:128] = x[m,h,:512] . W_UV[h]`` (vLLM page, "Layout and topology
-  behavior": the UV projection beside the fused query path).
+  behavior": the UV projection beside the fused query path);
+* ``mlaq_attn_*``         -- dense MLA decode attention over a paged latent
+  cache, split into ranges whose partials are stored as BF16 or FP32 and
+  merged into a BF16 output (b12x PR #441 "Allow FP32 split partials in
+  prepared dense MLA", commit text and "Behavior").
 """
 
 from __future__ import annotations
@@ -41,6 +45,11 @@ NOPE_DIM_GLM = 192
 V_DIM = 128
 ROW = LATENT_DIM + ROPE_DIM
 MX_BLOCK = 32
+MLAQ_PARTIAL_BF16, MLAQ_PARTIAL_FP32 = 0, 1
+MLAQ_ATTN_ROW = ROW
+MLAQ_ATTN_MAX_HEADS = 16
+MLAQ_ATTN_MAX_SPLITS = 256
+MLAQ_ATTN_SPLIT_ALIGN = 64
 
 _STATUS_NAMES = {0: "MLAQ_OK", 1: "MLAQ_ERR_UNSUPPORTED", 2: "MLAQ_ERR_INVALID_ARG", 3: "MLAQ_ERR_DEVICE"}
 
@@ -54,6 +63,17 @@ class RunArgs(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("out_stride_m", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
                 ("M", ctypes.c_int), ("H", ctypes.c_int), ("nope_dim", ctypes.c_int),
                 ("weight_format", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+class AttnArgs(ctypes.Structure):
+    """Mirror of ``mlaq_attn_args`` in include/mlaq.h (same field order and types)."""
+
+    _fields_ = [("q", ctypes.c_void_p), ("q_stride_m", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("kv_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("softmax_scale", ctypes.c_float),
+                ("M", ctypes.c_int), ("H", ctypes.c_int), ("page_size", ctypes.c_int), ("num_pages", ctypes.c_int),
+                ("block_table_stride", ctypes.c_int), ("num_splits", ctypes.c_int), ("partial_dtype", ctypes.c_int)]
 
 
 class MlaqError(RuntimeError):
@@ -93,6 +113,18 @@ def library() -> ctypes.CDLL:
         lib.mlaq_uv_prewarm.restype = I
         lib.mlaq_uv_run.argtypes = [P, P, P, P, I, I, I, P]
         lib.mlaq_uv_run.restype = I
+        lib.mlaq_attn_workspace_size.argtypes = [I, I, I, I]
+        lib.mlaq_attn_workspace_size.restype = ctypes.c_size_t
+        lib.mlaq_attn_num_splits.argtypes = [I, I, I, ctypes.POINTER(I)]
+        lib.mlaq_attn_num_splits.restype = I
+        lib.mlaq_attn_plan_supported.argtypes = [I, I, I, I, ctypes.c_char_p]
+        lib.mlaq_attn_plan_supported.restype = I
+        lib.mlaq_attn_can_implement.argtypes = [I] * 5
+        lib.mlaq_attn_can_implement.restype = I
+        lib.mlaq_attn_prewarm.argtypes = [I, I]
+        lib.mlaq_attn_prewarm.restype = I
+        lib.mlaq_attn_run.argtypes = [ctypes.POINTER(AttnArgs), P]
+        lib.mlaq_attn_run.restype = I
         lib.mlaq_last_error.argtypes = []
         lib.mlaq_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -286,3 +318,88 @@ def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor |
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _check(library().mlaq_uv_run(_ptr(x), _ptr(w_uv), _ptr(w_uv_scales), _ptr(out), M, H, weight_format,
                                  ctypes.c_void_p(s.cuda_stream)))
+
+
+def mlaq_attn_workspace_size(M: int, H: int, num_splits: int, partial_dtype: int = MLAQ_PARTIAL_BF16) -> int:
+    """Workspace bytes of an attention plan (0 for one split or an invalid plan)."""
+    return int(library().mlaq_attn_workspace_size(M, H, num_splits, partial_dtype))
+
+
+def mlaq_attn_num_splits(M: int, max_seq_len: int, device=None) -> int:
+    """Split count that fills the device for M sequences of up to max_seq_len tokens."""
+    n = ctypes.c_int(0)
+    _check(library().mlaq_attn_num_splits(M, max_seq_len, _device_index(device), ctypes.byref(n)))
+    return n.value
+
+
+def mlaq_attn_plan_supported(num_heads: int, page_size: int, num_splits: int,
+                             partial_dtype: int = MLAQ_PARTIAL_BF16, arch: str = "gfx950") -> int:
+    """Status of the pure attention gate for an architecture name."""
+    return library().mlaq_attn_plan_supported(num_heads, page_size, num_splits, partial_dtype,
+                                              arch.encode() if arch is not None else None)
+
+
+def mlaq_attn_can_implement(num_heads: int, page_size: int, num_splits: int,
+                            partial_dtype: int = MLAQ_PARTIAL_BF16, device=None) -> bool:
+    return bool(library().mlaq_attn_can_implement(num_heads, page_size, num_splits, partial_dtype,
+                                                  _device_index(device)))
+
+
+def mlaq_attn_prewarm(partial_dtype: int = MLAQ_PARTIAL_BF16, device=None) -> None:
+    _check(library().mlaq_attn_prewarm(partial_dtype, _device_index(device)))
+
+
+def mlaq_attn_run(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                  out: torch.Tensor, softmax_scale: float, num_splits: int,
+                  partial_dtype: int = MLAQ_PARTIAL_BF16, workspace: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> None:
+    """Dense MLA decode attention: q bf16 [M,H,576] (a view whose last
+    dimension is contiguous), kv_cache bf16 [num_pages,page_size,576],
+    block_table int32 [M,max_blocks], seq_lens int32 [M], out bf16 [M,H,512],
+    lse fp32 [M,H] or None, workspace a uint8 tensor of at least
+    ``mlaq_attn_workspace_size`` bytes (None when that is 0)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [M,H,576]")
+    M, H = int(q.shape[0]), int(q.shape[1])
+    dev = q.device
+    q_sm, q_sh = _expect_view(q, "q", torch.bfloat16, (M, H, ROW), dev)
+    if kv_cache.dim() != 3:
+        raise ValueError("kv_cache must be [num_pages,page_size,576]")
+    num_pages, page_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    _expect(kv_cache, "kv_cache", torch.bfloat16, (num_pages, page_size, ROW), dev)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [M,max_blocks]")
+    _expect(block_table, "block_table", torch.int32, (M, int(block_table.shape[1])), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (M,), dev)
+    _expect(out, "out", torch.bfloat16, (M, H, LATENT_DIM), dev)
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (M, H), dev)
+    ws_bytes = 0
+    if workspace is not None:
+        if not workspace.is_contiguous() or workspace.device != dev:
+            raise ValueError("workspace must be a contiguous tensor on the query's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = AttnArgs(q.data_ptr(), q_sm, q_sh, kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                    out.data_ptr(), None if lse is None else lse.data_ptr(),
+                    None if workspace is None else workspace.data_ptr(), ws_bytes, float(softmax_scale),
+                    M, H, page_size, num_pages, int(block_table.shape[1]), int(num_splits), int(partial_dtype))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(library().mlaq_attn_run(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
+
+
+def dense_mla_decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, num_splits: int | None = None,
+                     partial_dtype: int = MLAQ_PARTIAL_BF16, max_seq_len: int | None = None, return_lse=False):
+    """Allocate the output (and workspace) and run one attention call. With
+    ``num_splits`` None the library's split heuristic picks it from
+    ``max_seq_len`` (read from ``seq_lens`` when not given: a device sync)."""
+    M, H = int(q.shape[0]), int(q.shape[1])
+    if num_splits is None:
+        if max_seq_len is None:
+            max_seq_len = int(seq_lens.max().item()) if M else 0
+        num_splits = mlaq_attn_num_splits(max(M, 1), max_seq_len, q.device)
+    out = torch.empty((M, H, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((M, H), dtype=torch.float32, device=q.device) if return_lse else None
+    n = mlaq_attn_workspace_size(M, H, num_splits, partial_dtype)
+    ws = torch.empty((n,), dtype=torch.uint8, device=q.device) if n else None
+    mlaq_attn_run(q, kv_cache, block_table, seq_lens, out, softmax_scale, num_splits, partial_dtype, ws, lse)
+    return (out, lse) if return_lse else out

@@ -115,6 +115,35 @@ bool rows_disjoint(int M, int H, int64_t sm, int64_t sh) {
   return (sh >= row && sm >= int64_t(H) * sh) || (sm >= row && sh >= int64_t(M) * sm);
 }
 
+bool known_partial(int d) { return d == MLAQ_PARTIAL_BF16 || d == MLAQ_PARTIAL_FP32; }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Workspace layout: partials [M,S,H,512] (bf16 or fp32) from offset 0, then
+// lse_s [M,S,H] fp32 from the next 256-byte boundary.
+size_t attn_lse_offset(int M, int H, int S, int partial_dtype) {
+  const size_t esz = partial_dtype == MLAQ_PARTIAL_FP32 ? 4 : 2;
+  return round256(size_t(M) * S * H * mlaq::kLatent * esz);
+}
+
+// Per-device compute-unit count, queried once.
+std::mutex g_cu_mu;
+int g_cus[kMaxDevices];
+
+int device_cus(int device, int* cus) {
+  if (device < 0 || device >= kMaxDevices) return fail(MLAQ_ERR_INVALID_ARG, "device ordinal %d out of range", device);
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (g_cus[device] == 0) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess || n < 1)
+      return fail(MLAQ_ERR_DEVICE, "compute-unit count of device %d: %s", device, hipGetErrorString(e));
+    g_cus[device] = n;
+  }
+  *cus = g_cus[device];
+  return MLAQ_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -324,6 +353,167 @@ int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* 
   mlaq::UvArgs ka{static_cast<const uint16_t*>(x), w_uv, static_cast<const uint8_t*>(w_uv_scales), out, M, H};
   void* kargs[] = {&ka};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Dense MLA decode attention
+// ---------------------------------------------------------------------------
+
+size_t mlaq_attn_workspace_size(int M, int H, int num_splits, int partial_dtype) {
+  if (M < 0 || M > mlaq::kAttnMaxM || H < 1 || H > mlaq::kAttnMaxHeads || num_splits < 1 ||
+      num_splits > mlaq::kAttnMaxSplits || !known_partial(partial_dtype))
+    return 0;
+  if (num_splits == 1) return 0;
+  return attn_lse_offset(M, H, num_splits, partial_dtype) + round256(size_t(M) * num_splits * H * sizeof(float));
+}
+
+int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits) {
+  clear_error();
+  if (!num_splits) return fail(MLAQ_ERR_INVALID_ARG, "num_splits is NULL");
+  if (M < 1 || max_seq_len < 0) return fail(MLAQ_ERR_INVALID_ARG, "M must be >= 1 and max_seq_len >= 0");
+  int cus = 0;
+  int st = device_cus(device, &cus);
+  if (st != MLAQ_OK) return st;
+  // Two split workgroups per compute unit (each holds one 74 KiB LDS tile),
+  // ranges of at least 256 tokens (four 64-token tiles).
+  long long want = 2LL * cus / M;
+  const long long by_len = (max_seq_len + 255) / 256;
+  if (want > by_len) want = by_len;
+  if (want > mlaq::kAttnMaxSplits) want = mlaq::kAttnMaxSplits;
+  *num_splits = want < 1 ? 1 : int(want);
+  return MLAQ_OK;
+}
+
+int mlaq_attn_plan_supported(int num_heads, int page_size, int num_splits, int partial_dtype, const char* arch) {
+  clear_error();
+  if (!arch) return fail(MLAQ_ERR_INVALID_ARG, "arch is NULL");
+  if (!known_partial(partial_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown partial_dtype %d", partial_dtype);
+  if (!is_gfx950(arch)) return fail(MLAQ_ERR_UNSUPPORTED, "device architecture '%s' is not gfx950", arch);
+  if (num_heads < 1 || num_heads > mlaq::kAttnMaxHeads)
+    return fail(MLAQ_ERR_UNSUPPORTED, "num_heads=%d outside 1..16", num_heads);
+  if (page_size < 1 || page_size > mlaq::kAttnMaxPage)
+    return fail(MLAQ_ERR_UNSUPPORTED, "page_size=%d outside 1..4096", page_size);
+  if (num_splits < 1 || num_splits > mlaq::kAttnMaxSplits)
+    return fail(MLAQ_ERR_UNSUPPORTED, "num_splits=%d outside 1..256", num_splits);
+  return MLAQ_OK;
+}
+
+int mlaq_attn_can_implement(int num_heads, int page_size, int num_splits, int partial_dtype, int device) {
+  clear_error();
+  const char* arch = nullptr;
+  if (device_arch(device, &arch) != MLAQ_OK) return 0;
+  return mlaq_attn_plan_supported(num_heads, page_size, num_splits, partial_dtype, arch) == MLAQ_OK;
+}
+
+int mlaq_attn_prewarm(int partial_dtype, int device) {
+  clear_error();
+  if (!known_partial(partial_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown partial_dtype %d", partial_dtype);
+  const char* arch = nullptr;
+  int st = device_arch(device, &arch);
+  if (st != MLAQ_OK) return st;
+  if (!is_gfx950(arch)) return fail(MLAQ_ERR_UNSUPPORTED, "device architecture '%s' is not gfx950", arch);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+  const void* fns[] = {mlaq::attn_split_kernel_for(partial_dtype, false), mlaq::attn_split_kernel_for(partial_dtype, true),
+                       mlaq::attn_merge_kernel_for(partial_dtype)};
+  for (const void* fn : fns) {
+    hipFuncAttributes attr;
+    if (e == hipSuccess) e = hipFuncGetAttributes(&attr, fn);
+  }
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading attention kernels: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
+int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
+  clear_error();
+  if (!args) return fail(MLAQ_ERR_INVALID_ARG, "args is NULL");
+  const mlaq_attn_args& a = *args;
+  if (!known_partial(a.partial_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown partial_dtype %d", a.partial_dtype);
+  if (a.H < 1 || a.H > mlaq::kAttnMaxHeads) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d outside 1..16", a.H);
+  if (a.page_size < 1 || a.page_size > mlaq::kAttnMaxPage)
+    return fail(MLAQ_ERR_UNSUPPORTED, "page_size=%d outside 1..4096", a.page_size);
+  if (a.num_splits < 1 || a.num_splits > mlaq::kAttnMaxSplits)
+    return fail(MLAQ_ERR_UNSUPPORTED, "num_splits=%d outside 1..256", a.num_splits);
+  if (a.M < 0 || a.M > mlaq::kAttnMaxM) return fail(MLAQ_ERR_UNSUPPORTED, "M=%d outside 0..65536", a.M);
+  if (a.M == 0) return MLAQ_OK;
+  if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out)
+    return fail(MLAQ_ERR_INVALID_ARG, "q, kv_cache, block_table, seq_lens and out must be non-NULL");
+  if (a.num_pages < 1 || a.block_table_stride < 1)
+    return fail(MLAQ_ERR_INVALID_ARG, "num_pages and block_table_stride must be >= 1");
+  if (int64_t(a.block_table_stride) * a.page_size > (int64_t(1) << 30))
+    return fail(MLAQ_ERR_UNSUPPORTED, "block_table_stride * page_size exceeds 2^30 tokens");
+  if (!(a.softmax_scale == a.softmax_scale) || a.softmax_scale > 3.4e38f || a.softmax_scale < -3.4e38f)
+    return fail(MLAQ_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (a.q_stride_m < 0 || a.q_stride_h < 0 || a.q_stride_m % 8 || a.q_stride_h % 8)
+    return fail(MLAQ_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements");
+  if (!aligned(a.q, 16) || !aligned(a.kv_cache, 16) || !aligned(a.out, 16))
+    return fail(MLAQ_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+  if (!aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.lse, 4))
+    return fail(MLAQ_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+  const size_t ws = mlaq_attn_workspace_size(a.M, a.H, a.num_splits, a.partial_dtype);
+  if (ws > 0 && (!a.workspace || a.workspace_bytes < ws))
+    return fail(MLAQ_ERR_INVALID_ARG, "workspace must hold %zu bytes", ws);
+  if (ws > 0 && !aligned(a.workspace, 256)) return fail(MLAQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  // Address spans: inputs and outputs must not overlap.
+  const size_t mh = size_t(a.M) * size_t(a.H);
+  const size_t q_bytes = size_t((int64_t(a.M) - 1) * a.q_stride_m + (int64_t(a.H) - 1) * a.q_stride_h + mlaq::kRow) * 2;
+  const size_t kv_bytes = size_t(a.num_pages) * size_t(a.page_size) * mlaq::kRow * 2;
+  const size_t bt_bytes = size_t(a.M) * size_t(a.block_table_stride) * 4;
+  const size_t sl_bytes = size_t(a.M) * 4;
+  const size_t out_bytes = mh * mlaq::kLatent * 2, lse_bytes = a.lse ? mh * 4 : 0;
+  const void* ins[] = {a.q, a.kv_cache, a.block_table, a.seq_lens};
+  const size_t in_bytes[] = {q_bytes, kv_bytes, bt_bytes, sl_bytes};
+  const void* outs[] = {a.out, a.lse, ws > 0 ? a.workspace : nullptr};
+  const size_t out_sizes[] = {out_bytes, lse_bytes, ws};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], out_sizes[o], ins[i], in_bytes[i]))
+        return fail(MLAQ_ERR_INVALID_ARG, "an output or the workspace overlaps an input buffer");
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], out_sizes[o], outs[o2], out_sizes[o2]))
+        return fail(MLAQ_ERR_INVALID_ARG, "out, lse and workspace must not overlap");
+  }
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  const char* arch = nullptr;
+  int st = device_arch(device, &arch);
+  if (st != MLAQ_OK) return st;
+  st = mlaq_attn_plan_supported(a.H, a.page_size, a.num_splits, a.partial_dtype, arch);
+  if (st != MLAQ_OK) return st;
+
+  mlaq::AttnArgs ka{};
+  ka.q = static_cast<const uint16_t*>(a.q);
+  ka.kv = static_cast<const uint16_t*>(a.kv_cache);
+  ka.bt = a.block_table;
+  ka.seq_lens = a.seq_lens;
+  ka.part = ws > 0 ? a.workspace : nullptr;
+  ka.part_lse = ws > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) +
+                                                 attn_lse_offset(a.M, a.H, a.num_splits, a.partial_dtype))
+                       : nullptr;
+  ka.out = static_cast<uint16_t*>(a.out);
+  ka.lse = a.lse;
+  ka.q_sm = size_t(a.q_stride_m);
+  ka.q_sh = size_t(a.q_stride_h);
+  ka.scale_log2 = float(double(a.softmax_scale) * 1.4426950408889634);
+  ka.M = a.M;
+  ka.H = a.H;
+  ka.P = a.page_size;
+  ka.num_pages = a.num_pages;
+  ka.bt_stride = a.block_table_stride;
+  ka.S = a.num_splits;
+  dim3 split_grid, merge_grid, block;
+  mlaq::attn_launch_shapes(a.M, a.H, a.num_splits, &split_grid, &merge_grid, &block);
+  void* kargs[] = {&ka};
+  const hipStream_t st_ = static_cast<hipStream_t>(stream);
+  const bool direct = a.num_splits == 1;
+  e = hipLaunchKernel(mlaq::attn_split_kernel_for(a.partial_dtype, direct), split_grid, block, kargs, 0, st_);
+  if (e == hipSuccess && !direct)
+    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype), merge_grid, block, kargs, 0, st_);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;
 }

@@ -1,0 +1,445 @@
+// mlaq_attn.hip -- gfx950 kernels of dense MLA decode attention with split
+// partials: the consumer of the 576-wide query row.
+//
+// For each decode token m (one sequence, T_m = seq_lens[m] cached tokens in a
+// paged latent cache) and head h, over the token range of split s:
+//
+//   s_t   = softmax_scale * q[m,h,0:576] . kv_t[0:576]      (key = whole row)
+//   o_s   = sum_t exp(s_t - L_s) kv_t[0:512] / sum_t exp(s_t - L_s)
+//   lse_s = L_s + log sum_t exp(s_t - L_s)
+//
+// stored as FP32 or BF16 partials, then merged into a BF16 output:
+//   o = sum_s exp(lse_s - L) o_s / sum_s exp(lse_s - L),  L = max_s lse_s.
+// (b12x PR #441 "Allow FP32 split partials in prepared dense MLA": commit
+// text, walkthrough and "Behavior" -- partials in FP32 or BF16, BF16 the
+// default, merge output BF16. The attention itself is the plain latent-space
+// reading: the key is the 512 latent + 64 rotary row, the value its latent
+// part, shared by all heads.) Range s covers tokens [s*chunk, (s+1)*chunk)
+// of the sequence, chunk = ceil(T/S) rounded up to 64, so every range starts
+// on a 64-token tile.
+//
+// Split kernel, one workgroup (4 waves) per (m, s), two workgroups per
+// compute unit (each holds one 74 KiB LDS tile), so one workgroup's compute
+// covers the other's waits. Heads are the 16 rows of
+// v_mfma_f32_16x16x32_bf16 (H <= 16; missing rows repeat head H-1 and are
+// never stored). Tokens go in 64-token tiles:
+//  - lane (j, g) of wave w loads token 16w + j of a tile: 16 bytes at byte
+//    offset 16(4kb + g) of its 1152-byte row for kb = 0..17, i.e. 64
+//    contiguous bytes of each of 16 rows per instruction; at the start of an
+//    iteration those registers are written row-major into the LDS tile and
+//    the next tile's loads are issued into them, so every tile has a whole
+//    iteration of compute to arrive; its page indices are fetched one tile
+//    earlier still;
+//  - scores: the B fragment of K^T for lane (j, g) is exactly that 16-byte
+//    chunk (8 consecutive dims of token j), so S[h, token] is 18 MFMAs with Q
+//    held in registers as A fragments;
+//  - online softmax in the log2 domain: the row max over the tile is reduced
+//    across the 16 lanes of a row with DPP and across the 4 waves through
+//    LDS; the running sums stay per lane until the end;
+//  - P (bf16) goes to LDS; wave w multiplies it by the value columns
+//    [128w, 128w+128): 2 k-blocks of 32 tokens x 8 column tiles. The value
+//    B fragments come from the row-major tile through the gfx950 LDS
+//    transpose read (two 8-byte reads per fragment), with no gathers.
+// Tokens past the range end are clamped to its last token (so every loaded
+// row is finite data of the sequence) and masked to -inf before the softmax.
+// Finally the running sums are reduced (DPP + LDS, fixed order), o_s = acc * (1/l)
+// and lse_s are written to the workspace, or -- with one split -- the BF16
+// output and lse directly (merging one partial is the identity).
+#include <math.h>
+
+#include "mlaq.h"
+#include "mlaq_device.h"
+#include "mlaq_internal.h"
+
+namespace mlaq {
+namespace {
+
+using namespace dev;
+
+constexpr int kAttnThreads = 256;           // 4 waves
+constexpr int kKb = kRow / 32;              // 18 k-blocks of the 576-wide score product
+constexpr int kVb = kLatent / 32;           // the first 16 of them are the value
+constexpr int kKPitch = 2 * kRow + 32;      // bytes per token row of an LDS tile (1184)
+constexpr int kTileBytes = kAttnTile * kKPitch;
+constexpr int kPPitch = kAttnTile + 8;      // bf16 per head row of the LDS P tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int kPartialBf16 = MLAQ_PARTIAL_BF16;
+constexpr int kPartialFp32 = MLAQ_PARTIAL_FP32;
+constexpr int kDirect = 2; // one split: write the final output
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// An LDS byte pointer as the operand type of the transpose read.
+__device__ __forceinline__ __attribute__((address_space(3))) v4i16_t* lds_v4i16(const uint8_t* p) {
+  return (__attribute__((address_space(3))) v4i16_t*)(
+      (__attribute__((address_space(3))) uint8_t*)(const_cast<uint8_t*>(p)));
+}
+
+// DPP lane exchange within rows of 16 lanes (float payload).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each 16
+
+// Max / sum over the 16 lanes of a DPP row; every lane gets the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = __builtin_fmaxf(v, dpp<kQuadXor1>(v));
+  v = __builtin_fmaxf(v, dpp<kQuadXor2>(v));
+  v = __builtin_fmaxf(v, dpp<kRowHalfMirror>(v));
+  return __builtin_fmaxf(v, dpp<kRowMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  return v + dpp<kRowMirror>(v);
+}
+
+// Token range [a, b) of split s of a sequence of T tokens.
+__device__ __forceinline__ void split_range(int T, int S, int s, int* a, int* b) {
+  int chunk = (T + S - 1) / S;
+  chunk = (chunk + kAttnTile - 1) / kAttnTile * kAttnTile;
+  const long long lo = (long long)s * chunk;
+  *a = lo < T ? int(lo) : T;
+  *b = lo + chunk < T ? int(lo + chunk) : T;
+}
+
+__device__ __forceinline__ int clamp_len(const AttnArgs& a, int m) {
+  const int T = a.seq_lens[m];
+  const long long cap = (long long)a.bt_stride * a.P;
+  return T < 0 ? 0 : (T > cap ? int(cap) : T);
+}
+
+template <int PD>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvt[kTileBytes]; // the current tile, row = token
+  __shared__ __attribute__((aligned(16))) uint16_t pt[16 * kPPitch];  // P tile (bf16), row = head
+  __shared__ float red[4][16];                                         // per-wave row max / sum
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int S = a.S;
+  const int m = blockIdx.x / S, s = blockIdx.x - (blockIdx.x / S) * S;
+  const int H = a.H;
+  const int T = clamp_len(a, m);
+  int ta, tb;
+  split_range(T, S, s, &ta, &tb);
+
+  if (ta >= tb) {
+    // Empty range (or empty sequence): lse_s = -inf, and the merge skips it.
+    if constexpr (PD == kDirect) {
+      for (int x = tid; x < H * kLatent / 8; x += kAttnThreads) {
+        const int h = x / (kLatent / 8), c = x - h * (kLatent / 8);
+        *reinterpret_cast<u32x4_t*>(a.out + (size_t(m) * H + h) * kLatent + 8 * c) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if (a.lse && tid < H) a.lse[size_t(m) * H + tid] = -INFINITY;
+    } else {
+      if (tid < H) a.part_lse[(size_t(m) * S + s) * H + tid] = -INFINITY;
+    }
+    return;
+  }
+
+  const int32_t* bt = a.bt + size_t(m) * a.bt_stride;
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
+  const int trow = 16 * w + j; // this lane's token within a tile
+  // This lane's token in the tile at t0, clamped into the range.
+  auto token = [&](int t0) { return t0 + trow < tb ? t0 + trow : tb - 1; };
+  // Its block-table entry (raw: clamped into the pool only where it is used,
+  // so the load's latency is not waited for until the next tile needs it).
+  auto page_of = [&](int t0) { return bt[token(t0) / a.P]; };
+  auto load_tile = [&](int t0, int page, u32x4_t (&r)[kKb]) {
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    const int tc = token(t0);
+    const uint64_t row = uint64_t(uint32_t(page)) * uint32_t(a.P) + uint32_t(tc % a.P);
+    const uint8_t* rp = kvb + row * (2 * kRow) + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) r[kb] = *reinterpret_cast<const u32x4_t*>(rp + 64 * kb);
+  };
+  auto stage_tile = [&](const u32x4_t (&r)[kKb]) {
+    uint8_t* dst = kvt + trow * kKPitch + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) *reinterpret_cast<u32x4_t*>(dst + 64 * kb) = r[kb];
+  };
+
+  // Q as A fragments: lane (i = j, g) holds q[m, min(i, H-1), 32kb + 8g .. +8].
+  u32x4_t qa[kKb];
+  {
+    const int hq = j < H ? j : H - 1;
+    const uint16_t* qrow = a.q + size_t(m) * a.q_sm + size_t(hq) * a.q_sh + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) qa[kb] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * kb);
+  }
+  // Prologue: as at the end of every iteration, the next tile's loads and
+  // the page of the one after are in flight (nothing older is, so the loop
+  // never waits for them early).
+  u32x4_t kr[kKb];
+  load_tile(ta, page_of(ta), kr);
+  int pg_next = ta + kAttnTile < tb ? page_of(ta + kAttnTile) : 0;
+
+  float m_run[4], l_run[4];
+  f32x4_t acc[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // P column of this lane's token (the k slot of the value product).
+  const int pslot = trow;
+  const float sl2 = a.scale_log2;
+
+  for (int t0 = ta; t0 < tb; t0 += kAttnTile) {
+    const uint8_t* tile = kvt;
+    // 0. Stage this tile (its loads had the whole previous iteration to
+    //    arrive) and start the loads of the next one.
+    stage_tile(kr);
+    if (t0 + kAttnTile < tb) {
+      load_tile(t0 + kAttnTile, pg_next, kr);
+      pg_next = t0 + 2 * kAttnTile < tb ? page_of(t0 + 2 * kAttnTile) : 0;
+    }
+    __syncthreads();
+    // 1. Scores S[h = 4g + r, token 16w + j] from the LDS tile.
+    f32x4_t sacc;
+    {
+      // Two independent accumulator chains (even and odd k-blocks), summed
+      // at the end, so consecutive MFMAs do not wait on each other.
+      const uint8_t* krow = tile + trow * kKPitch + 16 * g;
+      f32x4_t s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+        s2[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, qa[kb]),
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 64 * kb)), s2[kb & 1], 0, 0, 0);
+      sacc = s2[0] + s2[1];
+    }
+    // 2. Masked scores in the log2 domain; tile max per row.
+    const bool valid = t0 + trow < tb;
+    float sc[4], mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = valid ? sacc[r] * sl2 : -INFINITY;
+      mx[r] = row16_max(sc[r]);
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[w][4 * g + r] = mx[r];
+    }
+    __syncthreads();
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;
+      const float tmax = __builtin_fmaxf(__builtin_fmaxf(red[0][h], red[1][h]), __builtin_fmaxf(red[2][h], red[3][h]));
+      const float mn = __builtin_fmaxf(m_run[r], tmax); // finite: every tile holds a valid token
+      alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - mn);
+      m_run[r] = mn;
+      const float p = __builtin_amdgcn_exp2f(sc[r] - mn);
+      l_run[r] = l_run[r] * alpha[r] + p;
+      sc[r] = p;
+    }
+    // 3. P (bf16) into LDS in slot order; rescale the output accumulators.
+    {
+      const uint32_t p01 = bf16x2_rne(sc[0], sc[1]), p23 = bf16x2_rne(sc[2], sc[3]);
+      pt[(4 * g + 0) * kPPitch + pslot] = uint16_t(p01);
+      pt[(4 * g + 1) * kPPitch + pslot] = uint16_t(p01 >> 16);
+      pt[(4 * g + 2) * kPPitch + pslot] = uint16_t(p23);
+      pt[(4 * g + 3) * kPPitch + pslot] = uint16_t(p23 >> 16);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
+    __syncthreads();
+    // 4. O[:, 128w + 16ct + j] += P . V over the tile's two 32-token blocks.
+    //    B fragment of lane (j, g): V[token 32kb2 + 8g + e][128w + 16ct + j],
+    //    e = 0..7, as two LDS transpose reads (ds_read_b64_tr_b16): within a
+    //    16-lane group, output lane i gets element i%4 of the 8 bytes that
+    //    lane 4e + i/4 addresses, so lane 4e + q points at columns
+    //    16ct + 4q .. +3 of token 8g + e (and of 8g + 4 + e for the second).
+    {
+      const int e = j >> 2, q = j & 3;
+      const uint8_t* vsrc = tile + (8 * g + e) * kKPitch + 2 * (128 * w + 4 * q);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pt + j * kPPitch + 32 * kb2 + 8 * g);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const uint8_t* vp = vsrc + 32 * kb2 * kKPitch + 32 * ct;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vp));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vp + 4 * kKPitch));
+          const u32x4_t vb = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
+                                                            __builtin_bit_cast(bf16x8_t, vb), acc[ct], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads(); // the tile, P and the row maxima are free again
+  }
+
+  // Row sums: 16 lanes (DPP), then the 4 waves in order.
+  float lsum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(l_run[r]);
+  if (j == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[w][4 * g + r] = lsum[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    if (h >= H) continue;
+    const float l = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
+    const float lse = (m_run[r] + __builtin_amdgcn_logf(l)) * kLn2;
+    const float inv = 1.0f / l; // one division per row; the outputs take a product
+    if constexpr (PD == kDirect) {
+      uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent + 128 * w + j;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = uint16_t(bf16x2_rne(acc[ct][r] * inv, 0.f));
+      if (a.lse && w == 0 && j == 0) a.lse[size_t(m) * H + h] = lse;
+    } else {
+      const size_t prow = (size_t(m) * S + s) * H + h;
+      if constexpr (PD == kPartialFp32) {
+        float* orow = static_cast<float*>(a.part) + prow * kLatent + 128 * w + j;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = acc[ct][r] * inv;
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(a.part) + prow * kLatent + 128 * w + j;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = uint16_t(bf16x2_rne(acc[ct][r] * inv, 0.f));
+      }
+      if (w == 0 && j == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
+// Max / sum over the 256 threads of a workgroup (fixed order: DPP within
+// rows, then rows and waves through LDS); every thread gets the result.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* scratch) {
+  v = MAX ? row16_max(v) : row16_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if ((lane & 15) == 0) scratch[4 * w + (lane >> 4)] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = MAX ? __builtin_fmaxf(r, scratch[i]) : r + scratch[i];
+  __syncthreads();
+  return r;
+}
+
+// Merge: one workgroup per (m, h). Thread t first takes lse_t (t < S) to
+// form L and the weights exp(lse_t - L) in LDS; then thread (group k, 8
+// columns) accumulates the ranges s = k, k+4, ... (four loads in flight),
+// and the four groups' sums are added in order.
+template <int PD>
+__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float wts[kAttnMaxSplits];
+  __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) float acc_l[3][kLatent];
+  const int H = a.H, S = a.S;
+  const int m = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int tid = threadIdx.x;
+  const float* pl = a.part_lse + size_t(m) * S * H + h;
+  const float ls = tid < S ? pl[size_t(tid) * H] : -INFINITY;
+  const float L = block_reduce<true>(ls, red);
+  uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent;
+  if (L == -INFINITY) { // no tokens at all
+    if (tid < kLatent / 8) *reinterpret_cast<u32x4_t*>(orow + 8 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+    if (a.lse && tid == 0) a.lse[size_t(m) * H + h] = -INFINITY;
+    return;
+  }
+  const float wt = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls - L) * kLog2e);
+  if (tid < S) wts[tid] = wt;
+  const float wsum = block_reduce<false>(wt, red); // also orders the wts writes before the reads
+  const int grp = tid >> 6, c = 8 * (tid & 63);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const size_t stride = size_t(H) * kLatent; // elements between consecutive ranges
+  const size_t base = (size_t(m) * S * H + h) * kLatent + c;
+  for (int s0 = grp; s0 < S; s0 += 16) {
+    float wv[4];
+    f32x4_t v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + 4 * u;
+      const int sc = s < S ? s : 0; // range 0 always exists; the weight is then 0
+      wv[u] = s < S ? wts[s] : 0.f;
+      const size_t off = base + size_t(sc) * stride;
+      if constexpr (PD == kPartialFp32) {
+        v[u][0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off);
+        v[u][1] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off + 4);
+      } else {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part) + off);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          v[u][i][0] = __uint_as_float(b[2 * i] << 16);
+          v[u][i][1] = __uint_as_float(b[2 * i] & 0xFFFF0000u);
+          v[u][i][2] = __uint_as_float(b[2 * i + 1] << 16);
+          v[u][i][3] = __uint_as_float(b[2 * i + 1] & 0xFFFF0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (wv[u] != 0.f) { // a range without tokens holds no partial
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += wv[u] * v[u][0][i];
+          o[4 + i] += wv[u] * v[u][1][i];
+        }
+      }
+  }
+  if (grp > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc_l[grp - 1][c + i] = o[i];
+  }
+  __syncthreads();
+  if (grp == 0) {
+    u32x4_t res;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x0 = o[2 * i], x1 = o[2 * i + 1];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        x0 += acc_l[k][c + 2 * i];
+        x1 += acc_l[k][c + 2 * i + 1];
+      }
+      res[i] = bf16x2_rne(x0 / wsum, x1 / wsum);
+    }
+    *reinterpret_cast<u32x4_t*>(orow + c) = res;
+    if (a.lse && tid == 0) a.lse[size_t(m) * H + h] = L + __builtin_amdgcn_logf(wsum) * kLn2;
+  }
+}
+
+} // namespace
+
+const void* attn_split_kernel_for(int partial_dtype, bool direct) {
+  if (direct) return reinterpret_cast<const void*>(&attn_split_kernel<kDirect>);
+  if (partial_dtype == MLAQ_PARTIAL_FP32) return reinterpret_cast<const void*>(&attn_split_kernel<kPartialFp32>);
+  if (partial_dtype == MLAQ_PARTIAL_BF16) return reinterpret_cast<const void*>(&attn_split_kernel<kPartialBf16>);
+  return nullptr;
+}
+
+const void* attn_merge_kernel_for(int partial_dtype) {
+  if (partial_dtype == MLAQ_PARTIAL_FP32) return reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32>);
+  if (partial_dtype == MLAQ_PARTIAL_BF16) return reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16>);
+  return nullptr;
+}
+
+void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block) {
+  *split_grid = dim3(unsigned(M) * unsigned(S), 1, 1);
+  *merge_grid = dim3(unsigned(M) * unsigned(H), 1, 1);
+  *block = dim3(kAttnThreads, 1, 1);
+}
+
+} // namespace mlaq

@@ -58,6 +58,34 @@ struct UvArgs {
 const void* uv_kernel_for(int weight_format, int m_tiles);
 void uv_launch_shape(int H, dim3* grid, dim3* block);
 
+// Dense MLA decode attention (all tensors contiguous in their inner
+// dimension; q rows strided).
+constexpr int kAttnTile = 64;       // tokens per kernel iteration = split alignment
+constexpr int kAttnMaxHeads = 16;   // heads are the 16 rows of one MFMA tile
+constexpr int kAttnMaxSplits = 256;
+constexpr int kAttnMaxPage = 4096;  // tokens per cache page
+constexpr int kAttnMaxM = 65536;
+
+struct AttnArgs {
+  const uint16_t* q;        // bf16 [M,H,576] at (q_sm, q_sh, 1)
+  const uint16_t* kv;       // bf16 [num_pages, P, 576], contiguous
+  const int32_t* bt;        // [M, bt_stride]: physical page of each block of P tokens
+  const int32_t* seq_lens;  // [M]
+  void* part;               // workspace: partials [M,S,H,512] (bf16 or fp32)
+  float* part_lse;          // workspace: lse_s [M,S,H] (natural log)
+  uint16_t* out;            // bf16 [M,H,512], contiguous
+  float* lse;               // optional [M,H]
+  size_t q_sm, q_sh;        // elements
+  float scale_log2;         // softmax_scale * log2(e)
+  int M, H, P, num_pages, bt_stride, S;
+};
+
+// Split kernel (per partial dtype, or the direct one-split form) and merge
+// kernel, and their launch shapes.
+const void* attn_split_kernel_for(int partial_dtype, bool direct);
+const void* attn_merge_kernel_for(int partial_dtype);
+void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block);
+
 // Host function pointer of the kernel for a variant (null if none).
 const void* kernel_for(const Variant& v);
 // Launch geometry of a variant for H heads.

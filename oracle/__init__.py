@@ -91,7 +91,7 @@ def _declare(lib):
     lib.mlaq_oracle_uv_run.argtypes = [P, P, P, P] + [ctypes.c_int] * 5 + [P, P]
     lib.mlaq_oracle_attn_run.restype = ctypes.c_int
     lib.mlaq_oracle_attn_run.argtypes = ([P, P, P, P] + [ctypes.c_int] * 7 + [ctypes.c_double]
-                                         + [ctypes.c_int] * 2 + [P] * 7 + [ctypes.c_int])
+                                         + [ctypes.c_int] * 2 + [P] * 8 + [ctypes.c_int])
     lib.mlaq_oracle_qscale.restype = ctypes.c_float
     lib.mlaq_oracle_qscale.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t]
     for name in ("mlaq_oracle_bf16_round", "mlaq_oracle_e4m3_encode", "mlaq_oracle_e4m3_decode",
@@ -220,7 +220,8 @@ def attention(q, kv, block_table, seq_lens, *, softmax_scale, num_splits=0, part
     ``diagnostics``, ``o`` (fp64 merged output before rounding), ``lse``
     (``[M,H]``), ``vabs`` (sum_t p_t |v_t|, ``[M,H,dv]``), ``smag`` (max_t of
     scale * sum_d |q_d kv_t[d]|, ``[M,H]``) and, when split, ``part``
-    (``[M,S,H,dv]``) and ``plse`` (``[M,S,H]``): the stored partials.
+    (``[M,S,H,dv]``) and ``plse`` (``[M,S,H]``), the stored partials, and
+    ``pvabs`` (``[M,S,H,dv]``: sum_t p_t |v_t| within each range).
     """
     lib = _load(lib_path)
     q = _c(q, np.uint16)
@@ -234,7 +235,7 @@ def attention(q, kv, block_table, seq_lens, *, softmax_scale, num_splits=0, part
     if block_table.ndim != 2 or block_table.shape[0] != M or seq_lens.shape != (M,):
         raise OracleError("block_table must be [M,max_blocks] and seq_lens [M]")
     out = np.zeros((M, H, dv), np.uint16)
-    o = lse = vabs = smag = part = plse = None
+    o = lse = vabs = smag = part = plse = pvabs = None
     if diagnostics:
         o = np.zeros((M, H, dv), np.float64)
         lse = np.zeros((M, H), np.float64)
@@ -243,17 +244,18 @@ def attention(q, kv, block_table, seq_lens, *, softmax_scale, num_splits=0, part
         if num_splits > 0:
             part = np.zeros((M, num_splits, H, dv), np.float64)
             plse = np.zeros((M, num_splits, H), np.float64)
+            pvabs = np.zeros((M, num_splits, H, dv), np.float64)
     rc = lib.mlaq_oracle_attn_run(_ptr(q), _ptr(kv), _ptr(block_table), _ptr(seq_lens), M, H, D, int(dv), P,
                                   num_pages, block_table.shape[1], float(softmax_scale), int(num_splits),
                                   int(partial_dtype), _ptr(out), _ptr(o), _ptr(lse), _ptr(vabs), _ptr(smag),
-                                  _ptr(part), _ptr(plse), int(threads))
+                                  _ptr(part), _ptr(plse), _ptr(pvabs), int(threads))
     if rc != 0:
         raise OracleError(f"mlaq_oracle_attn_run failed with status {rc}")
     res = {"out": out}
     if diagnostics:
         res.update(o=o, lse=lse, vabs=vabs, smag=smag)
         if num_splits > 0:
-            res.update(part=part, plse=plse)
+            res.update(part=part, plse=plse, pvabs=pvabs)
     return res
 
 

@@ -481,7 +481,8 @@ typedef struct {
   double* smag_out;   /* optional [M,H]: max_t softmax_scale * sum_d |q_d kv_t[d]| */
   double* part_out;   /* optional [M,S,H,DV]: stored partials (after rounding) */
   double* plse_out;   /* optional [M,S,H]: stored lse_s (fp32 values) */
-  int next_item;      /* work counter over m, under the lock */
+  double* pvabs_out;  /* optional [M,S,H,DV]: sum_t p_t |kv_t[d]| within each range */
+  int next_item;      /* work counter over (m, h) pairs, under the lock */
   pthread_mutex_t lock;
 } attn_job;
 
@@ -491,27 +492,34 @@ static const uint16_t* attn_row(const attn_job* j, int m, int t) {
   return j->kv + ((size_t)page * j->P + (size_t)(t % j->P)) * j->D;
 }
 
-/* Softmax over tokens [a, b) of one (m, h): normalized output into o[DV],
- * returns lse. Scores s[] are the precomputed s_t of the whole sequence. */
-static double attn_range(const attn_job* j, int m, const double* s, int a, int b, double* o) {
+/* Softmax over tokens [a, b) of one (m, h): normalized output into o[DV]
+ * (and, if vabs is given, the same weights applied to |kv_t[d]|), returns
+ * lse. Scores s[] are the precomputed s_t of the whole sequence. */
+static double attn_range(const attn_job* j, int m, const double* s, int a, int b, double* o, double* vabs) {
   double L = -INFINITY, sum = 0.0;
   for (int t = a; t < b; ++t)
     if (s[t] > L) L = s[t];
   for (int d = 0; d < j->DV; ++d) o[d] = 0.0;
+  if (vabs)
+    for (int d = 0; d < j->DV; ++d) vabs[d] = 0.0;
   for (int t = a; t < b; ++t) {
     double e = exp(s[t] - L);
     const uint16_t* row = attn_row(j, m, t);
     sum += e;
     for (int d = 0; d < j->DV; ++d) o[d] += e * (double)bf16_to_f32(row[d]);
+    if (vabs)
+      for (int d = 0; d < j->DV; ++d) vabs[d] += e * fabs((double)bf16_to_f32(row[d]));
   }
   for (int d = 0; d < j->DV; ++d) o[d] /= sum;
+  if (vabs)
+    for (int d = 0; d < j->DV; ++d) vabs[d] /= sum;
   return L + log(sum);
 }
 
-static void attn_sequence(attn_job* j, int m, double* s, double* o, double* ps) {
+static void attn_head(attn_job* j, int m, int h, double* s, double* o, double* ps) {
   const int H = j->H, D = j->D, DV = j->DV, T = j->seq_lens[m];
   const int S = j->num_splits;
-  for (int h = 0; h < H; ++h) {
+  {
     const uint16_t* qr = j->q + ((size_t)m * H + h) * D;
     const size_t orow = ((size_t)m * H + h) * DV;
     double smag = 0.0;
@@ -554,7 +562,7 @@ static void attn_sequence(attn_job* j, int m, double* s, double* o, double* ps) 
       }
     } else if (S == 0) {
       /* Step 2 without splitting: the definition itself. */
-      lse = attn_range(j, m, s, 0, T, o);
+      lse = attn_range(j, m, s, 0, T, o, NULL);
     } else {
       /* Step 2: one normalized partial per range, stored in its dtype. */
       int chunk = (T + S - 1) / S;
@@ -568,7 +576,8 @@ static void attn_sequence(attn_job* j, int m, double* s, double* o, double* ps) 
           plse[sp] = -INFINITY;
           for (int d = 0; d < DV; ++d) po[d] = 0.0;
         } else {
-          plse[sp] = attn_range(j, m, s, (int)a, (int)b, po);
+          double* pv = j->pvabs_out ? j->pvabs_out + (((size_t)m * S + sp) * H + h) * DV : NULL;
+          plse[sp] = attn_range(j, m, s, (int)a, (int)b, po, pv);
           if (j->partial_dtype != ORACLE_PARTIAL_EXACT) plse[sp] = (double)(float)plse[sp];
           for (int d = 0; d < DV; ++d) {
             if (j->partial_dtype == ORACLE_PARTIAL_BF16)
@@ -614,10 +623,10 @@ static void* attn_worker(void* arg) {
   if (s && o && ps)
     for (;;) {
       pthread_mutex_lock(&j->lock);
-      int m = j->next_item++;
+      int item = j->next_item++;
       pthread_mutex_unlock(&j->lock);
-      if (m >= j->M) break;
-      attn_sequence(j, m, s, o, ps);
+      if (item >= j->M * j->H) break;
+      attn_head(j, item / j->H, item % j->H, s, o, ps);
     }
   int failed = !(s && o && ps);
   free(s);
@@ -632,14 +641,14 @@ static void* attn_worker(void* arg) {
  * with partials stored per partial_dtype (0 BF16, 1 FP32, 2 kept in double).
  * Returns 0, or 1 on bad sizes or modes, 2 on missing buffers, 3 on host
  * allocation failure, 4 on a block-table entry or sequence length outside the
- * cache. Sequences are independent and split over `nthreads` threads; results
- * do not depend on the thread count.
+ * cache. (Sequence, head) pairs are independent and split over `nthreads`
+ * threads; results do not depend on the thread count.
  */
 int mlaq_oracle_attn_run(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
                          const int32_t* seq_lens, int M, int H, int D, int DV, int P, int num_pages,
                          int max_blocks, double softmax_scale, int num_splits, int partial_dtype,
                          uint16_t* out, double* o_out, double* lse_out, double* vabs_out, double* smag_out,
-                         double* part_out, double* plse_out, int nthreads) {
+                         double* part_out, double* plse_out, double* pvabs_out, int nthreads) {
   attn_job j;
   if (M < 0 || H < 0 || D < 1 || DV < 1 || DV > D || P < 1 || num_pages < 0 || max_blocks < 0) return 1;
   if (num_splits < 0 || partial_dtype < ORACLE_PARTIAL_BF16 || partial_dtype > ORACLE_PARTIAL_EXACT) return 1;
@@ -676,9 +685,10 @@ int mlaq_oracle_attn_run(const uint16_t* q, const uint16_t* kv, const int32_t* b
   j.smag_out = smag_out;
   j.part_out = num_splits > 0 ? part_out : NULL;
   j.plse_out = num_splits > 0 ? plse_out : NULL;
+  j.pvabs_out = num_splits > 0 ? pvabs_out : NULL;
   pthread_mutex_init(&j.lock, NULL);
   if (nthreads < 1) nthreads = 1;
-  if (nthreads > M) nthreads = M;
+  if (nthreads > M * H) nthreads = M * H;
   int status = 0;
   if (nthreads == 1) {
     if (attn_worker(&j)) status = 3;

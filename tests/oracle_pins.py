@@ -583,6 +583,8 @@ def check_attn_splits(lib=None):
         part = (e @ rows[a:b, :512]) / e.sum(axis=1, keepdims=True)
         assert np.allclose(r["plse"][0, s], lse, rtol=1e-12, atol=1e-12), f"range {s}: lse_s"
         assert np.allclose(r["part"][0, s], part, rtol=1e-12, atol=1e-14), f"range {s}: partial"
+        pv = (e @ np.abs(rows[a:b, :512])) / e.sum(axis=1, keepdims=True)
+        assert np.allclose(r["pvabs"][0, s], pv, rtol=1e-12, atol=1e-14), f"range {s}: sum p|v|"
     assert np.all(np.isneginf(r["plse"][0, 2])), "third range of T=200, S=3 is empty"
     # storage dtypes
     f32 = _attn(inp, lib, num_splits=5, partial_dtype=oracle.PARTIAL_FP32)

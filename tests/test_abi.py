@@ -25,13 +25,16 @@ def lib():
 
 def declared_functions():
     text = HEADER.read_text()
-    return re.findall(r"^\s*(?:int|const char\s*\*)\s*(mlaq_\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(mlaq_\w+)\s*\(", text, re.M)
 
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"mlaq_plan_supported", "mlaq_can_implement", "mlaq_prewarm",
                                          "mlaq_run", "mlaq_run_ex", "mlaq_last_error", "mlaq_uv_plan_supported",
-                                         "mlaq_uv_can_implement", "mlaq_uv_prewarm", "mlaq_uv_run"}
+                                         "mlaq_uv_can_implement", "mlaq_uv_prewarm", "mlaq_uv_run",
+                                         "mlaq_attn_workspace_size", "mlaq_attn_num_splits",
+                                         "mlaq_attn_plan_supported", "mlaq_attn_can_implement", "mlaq_attn_prewarm",
+                                         "mlaq_attn_run"}
 
 
 def test_library_exports_every_declared_function(lib):
@@ -252,3 +255,133 @@ def test_uv_run_rejects_before_any_device_call(lib, kw, status, msg):
 
 def test_uv_empty_batch_is_a_noop(lib):
     assert uv_run(lib, x=None, w=None, out=None, M=0) == OK
+
+
+# --------------------------------------------------------------------------
+# Dense MLA decode attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h", [1, 8, 11, 16])
+@pytest.mark.parametrize("page,splits", [(1, 1), (64, 16), (4096, 256)])
+@pytest.mark.parametrize("pd", [0, 1])
+def test_attn_gate_accepts(lib, h, page, splits, pd):
+    assert mq.mlaq_attn_plan_supported(h, page, splits, pd) == OK
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((0, 64, 4, 0), UNS, "num_heads=0"),
+    ((17, 64, 4, 0), UNS, "num_heads=17"),
+    ((16, 0, 4, 0), UNS, "page_size=0"),
+    ((16, 4097, 4, 0), UNS, "page_size=4097"),
+    ((16, 64, 0, 0), UNS, "num_splits=0"),
+    ((16, 64, 257, 0), UNS, "num_splits=257"),
+    ((16, 64, 4, 2), INV, "partial_dtype"),
+])
+def test_attn_gate_rejects(lib, args, status, msg):
+    assert mq.mlaq_attn_plan_supported(*args) == status
+    assert msg in mq.mlaq_last_error()
+    assert mq.mlaq_attn_plan_supported(16, 64, 4, 0, arch="gfx942") == UNS
+    assert mq.mlaq_attn_plan_supported(16, 64, 4, 0, arch=None) == INV
+
+
+def test_attn_workspace_size(lib):
+    def r256(n):
+        return (n + 255) // 256 * 256
+
+    for M, H, S, pd in ((32, 16, 16, 0), (32, 16, 16, 1), (3, 11, 5, 0), (1, 1, 256, 1)):
+        esz = 4 if pd else 2
+        assert mq.mlaq_attn_workspace_size(M, H, S, pd) == r256(M * S * H * 512 * esz) + r256(M * S * H * 4)
+    assert mq.mlaq_attn_workspace_size(32, 16, 1, 0) == 0  # one split writes the output directly
+    for bad in ((32, 17, 4, 0), (32, 16, 0, 0), (32, 16, 257, 0), (32, 16, 4, 3), (-1, 16, 4, 0)):
+        assert mq.mlaq_attn_workspace_size(*bad) == 0
+
+
+ATTN_PROBE = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "mlaq.h"
+int main(void) {
+  printf("%zu", sizeof(mlaq_attn_args));
+#define F(x) printf(" %zu", offsetof(mlaq_attn_args, x));
+  F(q) F(q_stride_m) F(q_stride_h) F(kv_cache) F(block_table) F(seq_lens) F(out) F(lse) F(workspace)
+  F(workspace_bytes) F(softmax_scale) F(M) F(H) F(page_size) F(num_pages) F(block_table_stride) F(num_splits)
+  F(partial_dtype)
+  printf("\n");
+  return 0;
+}
+"""
+
+
+def test_attn_args_layout_matches_header(tmp_path):
+    import subprocess
+
+    src = tmp_path / "probe.c"
+    src.write_text(ATTN_PROBE)
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", f"-I{HEADER.parent}", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(mq.AttnArgs)] + [getattr(mq.AttnArgs, name).offset for name, _ in mq.AttnArgs._fields_]
+    assert got == want
+
+
+def attn_run(lib, **kw):
+    # q [4,16,576] at A (18 KiB pitch), kv 10 pages of 64 rows at 64A, table at 2A, lens at 3A, out at 4A,
+    # workspace at 8A: all disjoint, never dereferenced (every case fails validation first).
+    M, H, S = 4, 16, 4
+    a = mq.AttnArgs(A, 16 * 576, 576, 64 * A, 2 * A, 3 * A, 4 * A, None, 8 * A,
+                    mq.mlaq_attn_workspace_size(M, H, S, 0), 0.07, M, H, 64, 10, 8, S, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.mlaq_attn_run(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(partial_dtype=5), INV, "partial_dtype"),
+    (dict(H=0), UNS, "H=0"),
+    (dict(H=17), UNS, "H=17"),
+    (dict(page_size=0), UNS, "page_size=0"),
+    (dict(num_splits=0), UNS, "num_splits=0"),
+    (dict(num_splits=300), UNS, "num_splits=300"),
+    (dict(M=70000), UNS, "M=70000"),
+    (dict(q=None), INV, "non-NULL"),
+    (dict(kv_cache=None), INV, "non-NULL"),
+    (dict(block_table=None), INV, "non-NULL"),
+    (dict(seq_lens=None), INV, "non-NULL"),
+    (dict(out=None), INV, "non-NULL"),
+    (dict(num_pages=0), INV, "num_pages"),
+    (dict(block_table_stride=0), INV, "block_table_stride"),
+    (dict(block_table_stride=1 << 24, page_size=128), UNS, "2^30"),
+    (dict(softmax_scale=float("nan")), INV, "finite"),
+    (dict(softmax_scale=float("inf")), INV, "finite"),
+    (dict(q_stride_h=100), INV, "multiples of 8"),
+    (dict(q_stride_m=-8), INV, "multiples of 8"),
+    (dict(q=A + 8), INV, "16-byte aligned"),
+    (dict(kv_cache=64 * A + 4), INV, "16-byte aligned"),
+    (dict(out=4 * A + 2), INV, "16-byte aligned"),
+    (dict(block_table=2 * A + 2), INV, "4-byte aligned"),
+    (dict(lse=5 * A + 1), INV, "4-byte aligned"),
+    (dict(workspace=None), INV, "workspace must hold"),
+    (dict(workspace_bytes=1000), INV, "workspace must hold"),
+    (dict(workspace=8 * A + 128), INV, "256-byte aligned"),
+    (dict(out=64 * A + 4096), INV, "overlaps an input"),
+    (dict(workspace=A + 256), INV, "overlaps an input"),
+    (dict(lse=4 * A + 1024), INV, "must not overlap"),
+])
+def test_attn_run_rejects_before_any_device_call(lib, kw, status, msg):
+    assert attn_run(lib, **kw) == status
+    assert msg in mq.mlaq_last_error()
+
+
+def test_attn_run_null_args_and_empty_batch(lib):
+    assert lib.mlaq_attn_run(None, None) == INV
+    assert attn_run(lib, M=0, q=None, kv_cache=None, out=None) == OK
+    assert mq.mlaq_last_error() == ""
+
+
+def test_attn_num_splits_rejects_before_device(lib):
+    n = ctypes.c_int(0)
+    assert lib.mlaq_attn_num_splits(4, 100, 0, None) == INV
+    assert lib.mlaq_attn_num_splits(0, 100, 0, ctypes.byref(n)) == INV
+    assert lib.mlaq_attn_num_splits(4, -1, 0, ctypes.byref(n)) == INV
+    assert lib.mlaq_attn_num_splits(4, 100, 99, ctypes.byref(n)) == INV  # device ordinal out of range
+    assert lib.mlaq_attn_prewarm(7, 0) == INV

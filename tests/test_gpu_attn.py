@@ -1,0 +1,360 @@
+"""GPU parity of dense MLA decode attention with split partials
+(mlaq_attn_run) against the oracle's split procedure with the same split
+count and partial dtype (b12x PR #441 "Allow FP32 split partials in prepared
+dense MLA": partials in BF16 or FP32, BF16 output; its validation checks
+error against a higher-precision reference, graph replay and high cache-page
+indices).
+
+Bar, per output element, with o the oracle's merged result before the final
+rounding (double), vabs = sum_t p_t |v_t|, smag = max_t scale sum_d |q_d k_td|
+and u = 2^-24, gamma_n = n u / (1 - n u):
+  |gpu - o| <= ulp_bf16(o)                          final bf16 rounding
+             + max_s ulp_store(o_s)                 partial storage (a rounding flip)
+             + (2^-8 + 4 eps + 4 gamma_T') vabs     bf16 P (2^-9, doubled), score and
+                                                    accumulation errors
+             + 4 dlse vmax + 2^-20 max|o|           merge weights and fp32 merge
+with eps = 2 (gamma_576 + 2^-22) smag + 2^-21 the relative error of one
+softmax weight (fp32 score product, scale rounding, exp2), T' = T + 2 tiles
++ 8, dlse = 2^-20 (1 + |lse|) + 2 gamma_T' + eps, vmax = max |v|. The
+partials read back from the workspace meet the same bar per range, and per
+call rel-L2 ||gpu - o|| / ||o|| <= 4e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_decode_query_amd as mq
+import oracle
+from gpu_util import dev_bf16, out_bits, ulp_bf16
+from workloads import make_attn_inputs
+
+pytestmark = pytest.mark.gpu
+
+BF16P, FP32P = mq.MLAQ_PARTIAL_BF16, mq.MLAQ_PARTIAL_FP32
+U = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def ulp_f32(x):
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.ldexp(1.0, (np.maximum(e, -126) - 23).astype(np.int64))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+    mq.library()
+
+
+class Dev:
+    """Device copies of one AttnInputs."""
+
+    def __init__(self, inp, kv=None, table=None):
+        self.q = dev_bf16(inp.q)
+        self.kv = dev_bf16(inp.kv) if kv is None else kv
+        self.bt = torch.from_numpy(inp.block_table if table is None else table).cuda()
+        self.sl = torch.from_numpy(inp.seq_lens).cuda()
+        self.M, self.H = inp.M, inp.H
+
+
+def run_attn(d, scale, S, pd, q=None, with_ws=False):
+    """One call; returns out bits, lse and (optionally) the workspace tensor."""
+    out = torch.empty((d.M, d.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((d.M, d.H), dtype=torch.float32, device="cuda")
+    n = mq.mlaq_attn_workspace_size(d.M, d.H, S, pd)
+    ws = torch.empty((n,), dtype=torch.uint8, device="cuda") if n else None
+    mq.mlaq_attn_run(d.q if q is None else q, d.kv, d.bt, d.sl, out, scale, S, pd, ws, lse)
+    torch.cuda.synchronize()
+    res = (out_bits(out), lse.cpu().numpy().astype(np.float64))
+    return res + (ws,) if with_ws else res
+
+
+def read_partials(ws, M, H, S, pd):
+    """Partials [M,S,H,512] and lse_s [M,S,H] from the documented workspace layout."""
+    esz = 4 if pd == FP32P else 2
+    nb = M * S * H * 512 * esz
+    raw = ws.cpu().numpy()
+    with np.errstate(invalid="ignore"):  # ranges with no tokens leave their partials unwritten
+        return _decode_partials(raw, nb, M, H, S, pd)
+
+
+def _decode_partials(raw, nb, M, H, S, pd):
+    if pd == FP32P:
+        part = raw[:nb].view(np.float32).astype(np.float64)
+    else:
+        part = oracle.bf16_to_f32(raw[:nb].view(np.uint16)).astype(np.float64)
+    off = (nb + 255) // 256 * 256
+    plse = raw[off:off + M * S * H * 4].view(np.float32).astype(np.float64)
+    return part.reshape(M, S, H, 512), plse.reshape(M, S, H)
+
+
+def oracle_run(inp, S, pd):
+    return oracle.attention(inp.q, inp.kv, inp.block_table, inp.seq_lens, softmax_scale=inp.softmax_scale,
+                            num_splits=S, partial_dtype=pd, threads=16)
+
+
+def _terms(inp, ref):
+    T = inp.seq_lens.astype(np.float64)
+    tprime = T + 2 * 64 + 8
+    gT = np.array([gamma(t) for t in tprime])[:, None]
+    eps = 2 * (gamma(576) + 2.0 ** -22) * ref["smag"] + 2.0 ** -21  # [M,H]
+    vmax = float(np.max(np.abs(oracle.bf16_to_f32(inp.kv[..., :512]))))
+    return gT, eps, vmax
+
+
+def assert_attn_parity(gpu, gpu_lse, ref, inp, S, pd, what, ws=None):
+    gT, eps, vmax = _terms(inp, ref)
+    o = ref["o"]
+    got = oracle.bf16_to_f32(gpu).astype(np.float64)
+    live = inp.seq_lens > 0
+    upart = np.zeros_like(o)
+    lse_mag = np.abs(np.where(np.isfinite(ref["lse"]), ref["lse"], 0.0))
+    if S > 1:
+        ok = np.isfinite(ref["plse"])[..., None]
+        ustore = ulp_bf16(ref["part"]) if pd == BF16P else ulp_f32(ref["part"])
+        upart = np.max(np.where(ok, ustore, 0.0), axis=1)
+        lse_mag = np.maximum(lse_mag, np.max(np.abs(np.where(np.isfinite(ref["plse"]), ref["plse"], 0.0)), axis=1))
+    dlse = 2.0 ** -20 * (1 + lse_mag) + 2 * gT + eps  # [M,H]
+    bound = (ulp_bf16(o) + upart + (2.0 ** -8 + 4 * eps[..., None] + 4 * gT[..., None]) * ref["vabs"]
+             + 4 * dlse[..., None] * vmax + 2.0 ** -20 * np.max(np.abs(o)))
+    bad = ~(np.abs(got - o) <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} outputs outside the bound, first {np.argwhere(bad)[0]}: "
+                           f"gpu {got[bad][0]} oracle {o[bad][0]} bound {bound[bad][0]}")
+    if live.any():
+        rel = np.linalg.norm(got[live] - o[live]) / max(np.linalg.norm(o[live]), 1e-30)
+        assert rel <= 4e-3, f"{what}: rel-L2 {rel}"
+    # empty sequences: zeros and lse = -inf
+    assert np.all(gpu[~live] == 0), f"{what}: empty sequences must give 0"
+    assert np.all(np.isneginf(gpu_lse[~live])), f"{what}: empty sequences must give lse = -inf"
+    lerr = np.abs(gpu_lse[live] - ref["lse"][live])
+    assert np.all(lerr <= dlse[live]), f"{what}: lse off by {lerr.max()}"
+    if ws is not None and S > 1:
+        part, plse = read_partials(ws, inp.M, inp.H, S, pd)
+        ok = np.isfinite(ref["plse"])
+        assert np.array_equal(np.isneginf(plse), ~ok), f"{what}: empty ranges must store lse = -inf"
+        ustore = ulp_bf16(ref["part"]) if pd == BF16P else ulp_f32(ref["part"])
+        pb = ustore + (2.0 ** -8 + 4 * eps[:, None, :, None] + 4 * gT[:, :, None, None]) * ref["pvabs"]
+        pbad = ok[..., None] & ~(np.abs(part - ref["part"]) <= pb)
+        assert not pbad.any(), f"{what}: {int(pbad.sum())} partials outside the bound, first {np.argwhere(pbad)[0]}"
+        lb = 2.0 ** -20 * (1 + np.abs(np.where(ok, ref["plse"], 0))) + 2 * gT[:, :, None] + eps[:, None, :]
+        assert np.all(np.abs(plse[ok] - ref["plse"][ok]) <= lb[ok]), f"{what}: lse_s"
+
+
+_cache = {}
+
+
+def cached_inputs(seed, H, lens, P=64, **kw):
+    key = (seed, H, tuple(lens), P, tuple(sorted(kw.items())))
+    if key not in _cache:
+        _cache[key] = make_attn_inputs(seed, H, lens, page_size=P, **kw)
+    return _cache[key]
+
+
+RAGGED = [1, 63, 64, 65, 200, 0, 1000, 129]
+
+
+@pytest.mark.parametrize("pd", [BF16P, FP32P])
+@pytest.mark.parametrize("H", [8, 11, 16])
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_attn_parity_ragged(pd, H, S):
+    inp = cached_inputs(8000 + H, H, RAGGED)
+    d = Dev(inp)
+    gpu, lse, ws = run_attn(d, inp.softmax_scale, S, pd, with_ws=True)
+    assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"ragged H={H} S={S} pd={pd}", ws)
+
+
+@pytest.mark.parametrize("H,P,lens", [(1, 64, [300, 7, 64]), (5, 16, [300, 7, 64, 0]), (16, 1, [70, 3]),
+                                      (13, 128, [500, 129, 1]), (16, 48, [333, 97])])
+def test_attn_heads_and_page_sizes(H, P, lens):
+    inp = cached_inputs(8100 + H + P, H, lens, P=P)
+    d = Dev(inp)
+    for S, pd in ((1, BF16P), (4, BF16P), (4, FP32P)):
+        gpu, lse, ws = run_attn(d, inp.softmax_scale, S, pd, with_ws=True)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"H={H} P={P} S={S} pd={pd}", ws)
+
+
+def test_attn_decode_batch_full_size():
+    """The measured workload: 32 sequences of 4096 cached tokens, 16 heads,
+    the library's split count; both partial dtypes. Against the exact split
+    partials, FP32 storage errs clearly less than BF16 storage (over 4 M
+    values; the remaining FP32 error is the bf16 P operand of the value
+    product, about 2^-10 relative)."""
+    H, M, T = 16, 32, 4096
+    inp = cached_inputs(8200, H, [T] * M)
+    d = Dev(inp)
+    S = mq.mlaq_attn_num_splits(M, T)
+    assert S >= 2
+    exact = oracle_run(inp, S, oracle.PARTIAL_EXACT)
+    perr = {}
+    for pd in (BF16P, FP32P):
+        gpu, lse, ws = run_attn(d, inp.softmax_scale, S, pd, with_ws=True)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"full size pd={pd}", ws)
+        part, _ = read_partials(ws, M, H, S, pd)
+        perr[pd] = np.linalg.norm(part - exact["part"]) / np.linalg.norm(exact["part"])
+    assert perr[FP32P] < 0.75 * perr[BF16P], f"partial errors fp32 {perr[FP32P]} vs bf16 {perr[BF16P]}"
+
+
+def test_attn_long_context():
+    """One 65,536-token sequence (the pages' 64k-context decode), 16 heads."""
+    H, T = 16, 65536
+    inp = cached_inputs(8300, H, [T])
+    d = Dev(inp)
+    for S in (mq.mlaq_attn_num_splits(1, T), 1):
+        gpu, lse, ws = run_attn(d, inp.softmax_scale, S, BF16P, with_ws=True)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, BF16P), inp, S, BF16P, f"64k S={S}", ws)
+
+
+@pytest.mark.parametrize("S", [1, 2, 5])
+@pytest.mark.parametrize("pd", [BF16P, FP32P])
+def test_attn_structured_bit_exact(S, pd):
+    """q = 0 with every cached row equal: every weight is exactly 1 and every
+    partial and the output are that row. A single token gives its row."""
+    H = 16
+    inp = make_attn_inputs(8400, H, [256, 64, 1, 77])
+    inp.q[:2] = 0
+    row = inp.kv[inp.block_table[0, 0], 5].copy()
+    for m in range(2):
+        for b in range(int(math.ceil(inp.seq_lens[m] / 64))):
+            inp.kv[inp.block_table[m, b]] = row
+    gpu, _ = run_attn(Dev(inp), inp.softmax_scale, S, pd)
+    assert np.array_equal(gpu[:2], np.broadcast_to(row[:512], (2, H, 512))), "constant rows"
+    assert np.array_equal(gpu[2], np.broadcast_to(inp.kv[inp.block_table[2, 0], 0, :512], (H, 512))), "T = 1"
+    ref = oracle_run(inp, S, pd)
+    assert np.array_equal(gpu[:3], ref["out"][:3])
+
+
+def test_attn_high_page_indices():
+    """A 4.4 GB cache pool (byte offsets past 2^32) with the sequences' pages
+    placed at its top end."""
+    H = 16
+    inp = cached_inputs(8500, H, [1000, 64, 333])
+    n_pool = 60000
+    pool = torch.zeros((n_pool, 64, 576), dtype=torch.bfloat16, device="cuda")
+    used = np.unique(inp.block_table[inp.block_table >= 0])
+    remap = {int(p): n_pool - 1 - i for i, p in enumerate(used)}
+    for p, hp in remap.items():
+        pool[hp] = dev_bf16(inp.kv[p])
+    table = np.where(inp.block_table >= 0, np.vectorize(lambda x: remap.get(int(x), -1))(inp.block_table), -1)
+    d = Dev(inp, kv=pool, table=table.astype(np.int32))
+    for S, pd in ((1, BF16P), (6, FP32P)):
+        gpu, lse = run_attn(d, inp.softmax_scale, S, pd)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"high pages S={S}")
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_attn_strided_query():
+    """q inside the fused query's pitched workspace (640-element head pitch),
+    and a head-major [H,M,576] q passed as a transposed view."""
+    H = 11
+    inp = cached_inputs(8600, H, [130, 64, 7])
+    d = Dev(inp)
+    ref = oracle_run(inp, 3, BF16P)
+    ws = torch.zeros((inp.M, H, 640), dtype=torch.bfloat16, device="cuda")
+    ws[:, :, :576] = d.q
+    gpu, lse = run_attn(d, inp.softmax_scale, 3, BF16P, q=ws[:, :, :576])
+    assert_attn_parity(gpu, lse, ref, inp, 3, BF16P, "pitched q")
+    qhm = d.q.transpose(0, 1).contiguous()
+    gpu2, _ = run_attn(d, inp.softmax_scale, 3, BF16P, q=qhm.transpose(0, 1))
+    assert np.array_equal(gpu2, gpu), "head-major q view"
+
+
+def test_attn_device_values_are_clamped():
+    """A sequence length past the block table's capacity acts as the capacity;
+    table entries past the live blocks are never used."""
+    H = 8
+    inp = make_attn_inputs(8700, H, [128, 100], max_blocks=3)
+    inp.block_table[1, 2] = inp.block_table[0, 0]  # a live page for the clamped tail
+    d = Dev(inp)
+    sl = inp.seq_lens.copy()
+    sl[1] = 10 ** 6
+    d.sl = torch.from_numpy(sl).cuda()
+    got, lse = run_attn(d, inp.softmax_scale, 2, BF16P)
+    inp.seq_lens = np.array([128, 3 * 64], np.int32)  # what the library must have used
+    assert_attn_parity(got, lse, oracle_run(inp, 2, BF16P), inp, 2, BF16P, "clamped length")
+    wide = make_attn_inputs(8701, H, [128, 100], max_blocks=6)
+    d = Dev(wide)
+    base, _ = run_attn(d, wide.softmax_scale, 2, BF16P)
+    table = wide.block_table.copy()
+    table[table < 0] = 2 ** 30
+    d.bt = torch.from_numpy(table).cuda()
+    again, _ = run_attn(d, wide.softmax_scale, 2, BF16P)
+    assert np.array_equal(again, base)
+
+
+def test_attn_guard_bytes_and_determinism():
+    H = 16
+    inp = cached_inputs(8800, H, [500, 3, 0, 64])
+    d = Dev(inp)
+    S, pd = 4, FP32P
+    n = inp.M * H * 512
+    buf = torch.full((4096 + n + 4096,), 0x5A5A, dtype=torch.int16, device="cuda")
+    out = buf[4096:4096 + n].view(torch.bfloat16).view(inp.M, H, 512)
+    need = mq.mlaq_attn_workspace_size(inp.M, H, S, pd)
+    wsbuf = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    mq.mlaq_attn_run(d.q, d.kv, d.bt, d.sl, out, inp.softmax_scale, S, pd, wsbuf[:need])
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:4096] == 0x5A5A) and np.all(host[4096 + n:] == 0x5A5A), "out guard bytes"
+    assert np.all(wsbuf[need:].cpu().numpy() == 0xA5), "workspace tail"
+    first = out_bits(out)
+    again, _ = run_attn(d, inp.softmax_scale, S, pd)
+    assert np.array_equal(first, again)
+
+
+def test_attn_graph_replay_with_mutated_inputs():
+    """Capture split + merge once; change q, the cache and the lengths in
+    place; each replay matches an eager call bit for bit and the oracle."""
+    H, S, pd = 16, 4, BF16P
+    mq.mlaq_attn_prewarm(pd)
+    lens0 = [700, 64, 5]
+    pool = 40
+
+    def spare(lens):
+        return pool - sum((x + 63) // 64 for x in lens)
+
+    inp = make_attn_inputs(8900, H, lens0, max_blocks=16, spare_pages=spare(lens0))
+    d = Dev(inp)
+    out = torch.empty((inp.M, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((mq.mlaq_attn_workspace_size(inp.M, H, S, pd),), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st, capture_error_mode="global"):
+            mq.mlaq_attn_run(d.q, d.kv, d.bt, d.sl, out, inp.softmax_scale, S, pd, ws)
+    torch.cuda.synchronize()
+    for seed, lens in ((8900, lens0), (8901, [1000, 1, 333]), (8902, [64, 0, 1024])):
+        cur = make_attn_inputs(seed, H, lens, max_blocks=16, spare_pages=spare(lens))
+        d.q.copy_(dev_bf16(cur.q))
+        d.kv.copy_(dev_bf16(cur.kv))
+        d.bt.copy_(torch.from_numpy(cur.block_table))
+        d.sl.copy_(torch.from_numpy(cur.seq_lens))
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_bits(out)
+        eager, lse = run_attn(d, cur.softmax_scale, S, pd)
+        assert np.array_equal(got, eager), f"replay {seed} differs from eager"
+        assert_attn_parity(got, lse, oracle_run(cur, S, pd), cur, S, pd, f"replay {seed}")
+
+
+def test_attn_can_implement_and_split_heuristic():
+    assert mq.mlaq_attn_can_implement(16, 64, 16)
+    assert mq.mlaq_attn_can_implement(11, 1, 256, mq.MLAQ_PARTIAL_FP32)
+    assert not mq.mlaq_attn_can_implement(17, 64, 16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mq.mlaq_attn_num_splits(32, 4096) == min(2 * cus // 32, 16)
+    assert mq.mlaq_attn_num_splits(1, 65536) == min(2 * cus, 256)
+    assert mq.mlaq_attn_num_splits(4 * cus, 65536) == 1
+    assert mq.mlaq_attn_num_splits(32, 10) == 1
