@@ -418,7 +418,8 @@ int mlaq_attn_prewarm(int partial_dtype, int device) {
   hipError_t e = hipGetDevice(&cur);
   if (e == hipSuccess && cur != device) e = hipSetDevice(device);
   const void* fns[] = {mlaq::attn_split_kernel_for(partial_dtype, false), mlaq::attn_split_kernel_for(partial_dtype, true),
-                       mlaq::attn_merge_kernel_for(partial_dtype)};
+                       mlaq::attn_merge_kernel_for(partial_dtype, 2),
+                       mlaq::attn_merge_kernel_for(partial_dtype, mlaq::kAttnMaxSplits)};
   for (const void* fn : fns) {
     hipFuncAttributes attr;
     if (e == hipSuccess) e = hipFuncGetAttributes(&attr, fn);
@@ -513,7 +514,7 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   const bool direct = a.num_splits == 1;
   e = hipLaunchKernel(mlaq::attn_split_kernel_for(a.partial_dtype, direct), split_grid, block, kargs, 0, st_);
   if (e == hipSuccess && !direct)
-    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype), merge_grid, block, kargs, 0, st_);
+    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype, a.num_splits), merge_grid, block, kargs, 0, st_);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;
 }

@@ -323,101 +323,136 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   }
 }
 
-// Max / sum over the 256 threads of a workgroup (fixed order: DPP within
-// rows, then rows and waves through LDS); every thread gets the result.
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float v, float* scratch) {
-  v = MAX ? row16_max(v) : row16_sum(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if ((lane & 15) == 0) scratch[4 * w + (lane >> 4)] = v;
-  __syncthreads();
-  float r = scratch[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) r = MAX ? __builtin_fmaxf(r, scratch[i]) : r + scratch[i];
-  __syncthreads();
-  return r;
+// The value of `v` in lane `src` of the wave (ds_bpermute).
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-// Merge: one workgroup per (m, h). Thread t first takes lse_t (t < S) to
-// form L and the weights exp(lse_t - L) in LDS; then thread (group k, 8
-// columns) accumulates the ranges s = k, k+4, ... (four loads in flight),
-// and the four groups' sums are added in order.
-template <int PD>
+// Max / sum over the 64 lanes of a wave (DPP within rows, then across rows);
+// every lane gets the result, in the same order in every wave.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const int lane = threadIdx.x & 63;
+  v = __builtin_fmaxf(v, lane_value(v, lane ^ 16));
+  return __builtin_fmaxf(v, lane_value(v, lane ^ 32));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const int lane = threadIdx.x & 63;
+  v += lane_value(v, lane ^ 16);
+  return v + lane_value(v, lane ^ 32);
+}
+
+// Merge: one workgroup per (m, h, column part): QN parts of 512/QN columns
+// (QN = 4 from 32 ranges on, else 1). Thread t takes 8 columns (t % CG)
+// and the ranges s = t/CG + RG k. Every wave first requests the lse values,
+// then its first partials, and forms L = max_s lse_s and the weights
+// exp(lse_s - L) on its own (no workgroup barrier); the RG range groups'
+// sums are added in order at the end.
+template <int PD, int QN>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float wts[kAttnMaxSplits];
-  __shared__ float red[16];
-  __shared__ __attribute__((aligned(16))) float acc_l[3][kLatent];
+  constexpr int kMergeCols = kLatent / QN;                 // columns per workgroup
+  constexpr int CG = kMergeCols / 8;                       // column groups (8 columns each)
+  constexpr int RG = kAttnThreads / CG;                    // range groups
+  __shared__ float wts[4][kAttnMaxSplits];                 // each wave's copy of the weights
+  __shared__ __attribute__((aligned(16))) float part_sum[RG][kMergeCols];
+  constexpr int kFirst = 4;                                // ranges per thread requested up front
   const int H = a.H, S = a.S;
-  const int m = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const int tid = threadIdx.x;
-  const float* pl = a.part_lse + size_t(m) * S * H + h;
-  const float ls = tid < S ? pl[size_t(tid) * H] : -INFINITY;
-  const float L = block_reduce<true>(ls, red);
-  uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent;
-  if (L == -INFINITY) { // no tokens at all
-    if (tid < kLatent / 8) *reinterpret_cast<u32x4_t*>(orow + 8 * tid) = u32x4_t{0u, 0u, 0u, 0u};
-    if (a.lse && tid == 0) a.lse[size_t(m) * H + h] = -INFINITY;
-    return;
-  }
-  const float wt = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls - L) * kLog2e);
-  if (tid < S) wts[tid] = wt;
-  const float wsum = block_reduce<false>(wt, red); // also orders the wts writes before the reads
-  const int grp = tid >> 6, c = 8 * (tid & 63);
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int mh = blockIdx.x / QN, quarter = blockIdx.x - (blockIdx.x / QN) * QN;
+  const int m = mh / H, h = mh - (mh / H) * H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
+  const int c = kMergeCols * quarter + 8 * cg;
   const size_t stride = size_t(H) * kLatent; // elements between consecutive ranges
   const size_t base = (size_t(m) * S * H + h) * kLatent + c;
-  for (int s0 = grp; s0 < S; s0 += 16) {
-    float wv[4];
-    f32x4_t v[4][2];
+
+  // 1. lse values (lane l holds s = l + 64i), then this thread's first
+  //    ranges, all in flight before any wait.
+  const float* pl = a.part_lse + size_t(m) * S * H + h;
+  float lv[kAttnMaxSplits / 64];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + 4 * u;
-      const int sc = s < S ? s : 0; // range 0 always exists; the weight is then 0
-      wv[u] = s < S ? wts[s] : 0.f;
-      const size_t off = base + size_t(sc) * stride;
-      if constexpr (PD == kPartialFp32) {
-        v[u][0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off);
-        v[u][1] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off + 4);
-      } else {
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part) + off);
+  for (int i = 0; i < kAttnMaxSplits / 64; ++i) {
+    const int s = lane + 64 * i;
+    lv[i] = s < S ? pl[size_t(s) * H] : -INFINITY;
+  }
+  f32x4_t v[kFirst][2];
+  auto load_range = [&](int s, f32x4_t (&dst)[2]) {
+    const size_t off = base + size_t(s < S ? s : 0) * stride; // past S: range 0, weight 0
+    if constexpr (PD == kPartialFp32) {
+      dst[0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off);
+      dst[1] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off + 4);
+    } else {
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part) + off);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          v[u][i][0] = __uint_as_float(b[2 * i] << 16);
-          v[u][i][1] = __uint_as_float(b[2 * i] & 0xFFFF0000u);
-          v[u][i][2] = __uint_as_float(b[2 * i + 1] << 16);
-          v[u][i][3] = __uint_as_float(b[2 * i + 1] & 0xFFFF0000u);
-        }
+      for (int i = 0; i < 2; ++i) {
+        dst[i][0] = __uint_as_float(b[2 * i] << 16);
+        dst[i][1] = __uint_as_float(b[2 * i] & 0xFFFF0000u);
+        dst[i][2] = __uint_as_float(b[2 * i + 1] << 16);
+        dst[i][3] = __uint_as_float(b[2 * i + 1] & 0xFFFF0000u);
       }
     }
+  };
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (wv[u] != 0.f) { // a range without tokens holds no partial
+  for (int u = 0; u < kFirst; ++u) load_range(rg + RG * u, v[u]);
+
+  // 2. L and the weights, per wave.
+  float L = lv[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[i] += wv[u] * v[u][0][i];
-          o[4 + i] += wv[u] * v[u][1][i];
-        }
-      }
+  for (int i = 1; i < kAttnMaxSplits / 64; ++i) L = __builtin_fmaxf(L, lv[i]);
+  L = wave_max(L);
+  uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent;
+  if (L == -INFINITY) { // no tokens at all
+    if (rg == 0) *reinterpret_cast<u32x4_t*>(orow + c) = u32x4_t{0u, 0u, 0u, 0u};
+    if (a.lse && quarter == 0 && tid == 0) a.lse[size_t(m) * H + h] = -INFINITY;
+    return;
   }
-  if (grp > 0) {
+  float wsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc_l[grp - 1][c + i] = o[i];
+  for (int i = 0; i < kAttnMaxSplits / 64; ++i) {
+    const int s = lane + 64 * i;
+    const float wt = lv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lv[i] - L) * kLog2e);
+    if (s < S) wts[w][s] = wt;
+    wsum += wt;
   }
-  __syncthreads();
-  if (grp == 0) {
-    u32x4_t res;
+  wsum = wave_sum(wsum);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 3. Weighted sum of this thread's ranges.
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](int s, const f32x4_t (&x)[2]) {
+    if (s >= S) return;
+    const float wt = wts[w][s];
+    if (wt == 0.f) return; // a range without tokens holds no partial
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x0 = o[2 * i], x1 = o[2 * i + 1];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        x0 += acc_l[k][c + 2 * i];
-        x1 += acc_l[k][c + 2 * i + 1];
-      }
-      res[i] = bf16x2_rne(x0 / wsum, x1 / wsum);
+      o[i] += wt * x[0][i];
+      o[4 + i] += wt * x[1][i];
     }
-    *reinterpret_cast<u32x4_t*>(orow + c) = res;
-    if (a.lse && tid == 0) a.lse[size_t(m) * H + h] = L + __builtin_amdgcn_logf(wsum) * kLn2;
+  };
+#pragma unroll
+  for (int u = 0; u < kFirst; ++u) add(rg + RG * u, v[u]);
+  for (int s0 = rg + RG * kFirst; s0 < S; s0 += RG * kFirst) {
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) load_range(s0 + RG * u, v[u]);
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) add(s0 + RG * u, v[u]);
+  }
+
+  // 4. The range groups' sums, in order.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part_sum[rg][8 * cg + i] = o[i];
+  __syncthreads();
+  if (tid < kMergeCols / 2) {
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      x0 += part_sum[k][2 * tid];
+      x1 += part_sum[k][2 * tid + 1];
+    }
+    *reinterpret_cast<uint32_t*>(orow + kMergeCols * quarter + 2 * tid) = bf16x2_rne(x0 / wsum, x1 / wsum);
+    if (a.lse && quarter == 0 && tid == 0) a.lse[size_t(m) * H + h] = L + __builtin_amdgcn_logf(wsum) * kLn2;
   }
 }
 
@@ -430,15 +465,24 @@ const void* attn_split_kernel_for(int partial_dtype, bool direct) {
   return nullptr;
 }
 
-const void* attn_merge_kernel_for(int partial_dtype) {
-  if (partial_dtype == MLAQ_PARTIAL_FP32) return reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32>);
-  if (partial_dtype == MLAQ_PARTIAL_BF16) return reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16>);
+// Column parts of the merge for S ranges: four from 32 ranges on (more
+// workgroups, fewer ranges per thread), else one (fewer, fuller workgroups).
+int attn_merge_parts(int S) { return S >= 32 ? 4 : 1; }
+
+const void* attn_merge_kernel_for(int partial_dtype, int S) {
+  const bool q = attn_merge_parts(S) == 4;
+  if (partial_dtype == MLAQ_PARTIAL_FP32)
+    return q ? reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32, 4>)
+             : reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32, 1>);
+  if (partial_dtype == MLAQ_PARTIAL_BF16)
+    return q ? reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16, 4>)
+             : reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16, 1>);
   return nullptr;
 }
 
 void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block) {
   *split_grid = dim3(unsigned(M) * unsigned(S), 1, 1);
-  *merge_grid = dim3(unsigned(M) * unsigned(H), 1, 1);
+  *merge_grid = dim3(unsigned(M) * unsigned(H) * unsigned(attn_merge_parts(S)), 1, 1);
   *block = dim3(kAttnThreads, 1, 1);
 }
 

@@ -83,7 +83,7 @@ struct AttnArgs {
 // Split kernel (per partial dtype, or the direct one-split form) and merge
 // kernel, and their launch shapes.
 const void* attn_split_kernel_for(int partial_dtype, bool direct);
-const void* attn_merge_kernel_for(int partial_dtype);
+const void* attn_merge_kernel_for(int partial_dtype, int num_splits);
 void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block);
 
 // Host function pointer of the kernel for a variant (null if none).
