@@ -51,8 +51,9 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "µs per fused MLA query call + achieved HBM GB/s, H=16, M=1..32, BF16/MXFP8"
 HBM_PEAK_GBS = 8000.0
-# Sources whose hash the recorded HBM-traffic figure belongs to.
+# Sources whose hash the recorded HBM-traffic figures belong to.
 KERNEL_SOURCES = ("mlaq_kernels.hip", "mlaq_device.h", "mlaq_internal.h")
+ATTN_SOURCES = ("mlaq_attn.hip", "mlaq_device.h", "mlaq_internal.h")
 H, M_STEP, LAYERS, COPIES = 16, 32, 64, 6
 
 
@@ -70,6 +71,8 @@ def parse():
     p.add_argument("--no-pages-shape", action="store_true")
     p.add_argument("--no-uv", action="store_true")
     p.add_argument("--no-attention", action="store_true")
+    p.add_argument("--attention-only", action="store_true",
+                   help="run only the attention leg and print its JSON (for profiling; no bench line)")
     p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -512,9 +515,10 @@ def attention_leg(torch, mq, wl, args):
             us = time_graphs(torch, [g], max(4, args.steps // 2), max(2, args.warmup // 2),
                              per_step_units=copies) * 1e3
             gbs = nbytes / (us * 1e-6) / 1e9
+            traffic = measured_attn_traffic() if (idx == 0 and pd == mq.MLAQ_PARTIAL_BF16) else None
             row[tag] = {"us_per_call": round(us, 3), "gbs": round(gbs, 1),
                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
                         "workspace_bytes": n}
             log(f"[bench] attention {name}, {tag}, S={S}: {us:.2f} us/call, {gbs:.1f} GB/s "
                 f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
@@ -562,20 +566,30 @@ def cpu_baseline_leg(wl, layers, budget_s):
                       f"{t_used / n * 1e3:.2f} ms per layer"}
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the recorded PMC runs,
-    or None when the kernel sources changed since the counters were taken."""
+def _recorded(name, sources, key):
+    """A figure from a recorded PMC run under profiles/, or None when the
+    kernel sources changed since the counters were taken."""
     import hashlib
 
-    rec = ROOT / "profiles" / "fused_query_decode_step_traffic.txt"
+    rec = ROOT / "profiles" / name
     if not rec.exists():
         return None
     kv = dict(line.split(None, 1) for line in rec.read_text().splitlines() if line and not line.startswith("#"))
     csrc = ROOT / "mla_decode_query_amd" / "csrc"
-    h = hashlib.sha256(b"".join((csrc / f).read_bytes() for f in KERNEL_SOURCES))
+    h = hashlib.sha256(b"".join((csrc / f).read_bytes() for f in sources))
     if h.hexdigest() != kv.get("kernel_source_sha256", "").strip():
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    return int(kv[key])
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel (recorded PMC runs)."""
+    return _recorded("fused_query_decode_step_traffic.txt", KERNEL_SOURCES, "traffic_bytes_per_launch")
+
+
+def measured_attn_traffic():
+    """HBM bytes of one attention call on the decode batch (recorded PMC runs)."""
+    return _recorded("dense_mla_attention_traffic.txt", ATTN_SOURCES, "traffic_bytes_per_call")
 
 
 def main():
@@ -610,6 +624,9 @@ def main():
         log(f"[bench] calibration copy of {n} bytes done")
         return
     log(f"[bench] device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+    if args.attention_only:
+        print(json.dumps({"attention": attention_leg(torch, mq, wl, args)}), flush=True)
+        return
     step = decode_step_leg(torch, mq, wl, args)
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
     pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
