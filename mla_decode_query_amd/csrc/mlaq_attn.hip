@@ -43,8 +43,9 @@
 // Tokens past the range end are clamped to its last token (so every loaded
 // row is finite data of the sequence) and masked to -inf before the softmax.
 // Finally the running sums are reduced (DPP + LDS, fixed order), o_s = acc * (1/l)
-// and lse_s are written to the workspace, or -- with one split -- the BF16
-// output and lse directly (merging one partial is the identity).
+// goes through LDS so each lane stores 16 contiguous bytes, and o_s and lse_s
+// are written to the workspace, or -- with one split -- the BF16 output and lse
+// directly (merging one partial is the identity).
 #include <math.h>
 
 #include "mlaq.h"
@@ -168,13 +169,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     for (int kb = 0; kb < kKb; ++kb) *reinterpret_cast<u32x4_t*>(dst + 64 * kb) = r[kb];
   };
 
-  // Q as A fragments: lane (i = j, g) holds q[m, min(i, H-1), 32kb + 8g .. +8].
-  u32x4_t qa[kKb];
-  {
-    const int hq = j < H ? j : H - 1;
-    const uint16_t* qrow = a.q + size_t(m) * a.q_sm + size_t(hq) * a.q_sh + 8 * g;
+  // Q rows (16 heads, missing ones repeating head H-1) are read from memory
+  // once per workgroup, in 16-byte chunks spread over all threads, before the
+  // first tile's loads (so waiting for them never waits for the tile).
+  constexpr int kQChunks = 16 * kRow / 8;                          // 1152
+  constexpr int kQPerThread = (kQChunks + kAttnThreads - 1) / kAttnThreads; // 5
+  u32x4_t qc[kQPerThread];
 #pragma unroll
-    for (int kb = 0; kb < kKb; ++kb) qa[kb] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * kb);
+  for (int k = 0; k < kQPerThread; ++k) {
+    const int cidx = tid + kAttnThreads * k;
+    const int cc = cidx < kQChunks ? cidx : kQChunks - 1;
+    const int hh = cc / (kRow / 8), part = cc - hh * (kRow / 8);
+    const int hq = hh < H ? hh : H - 1;
+    qc[k] = *reinterpret_cast<const u32x4_t*>(a.q + size_t(m) * a.q_sm + size_t(hq) * a.q_sh + 8 * part);
   }
   // Prologue: as at the end of every iteration, the next tile's loads and
   // the page of the one after are in flight (nothing older is, so the loop
@@ -182,6 +189,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   u32x4_t kr[kKb];
   load_tile(ta, page_of(ta), kr);
   int pg_next = ta + kAttnTile < tb ? page_of(ta + kAttnTile) : 0;
+  // Q through the (still free) LDS tile into A fragments: lane (i = j, g)
+  // holds q[m, head i, 32kb + 8g .. +8].
+#pragma unroll
+  for (int k = 0; k < kQPerThread; ++k) {
+    const int cidx = tid + kAttnThreads * k;
+    if (cidx < kQChunks) {
+      const int hh = cidx / (kRow / 8), part = cidx - hh * (kRow / 8);
+      *reinterpret_cast<u32x4_t*>(kvt + hh * kKPitch + 16 * part) = qc[k];
+    }
+  }
+  __syncthreads();
+  u32x4_t qa[kKb];
+#pragma unroll
+  for (int kb = 0; kb < kKb; ++kb) qa[kb] = *reinterpret_cast<const u32x4_t*>(kvt + j * kKPitch + 16 * (4 * kb + g));
+  __syncthreads(); // the first staging overwrites the tile
 
   float m_run[4], l_run[4];
   f32x4_t acc[8];
@@ -254,10 +276,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       pt[(4 * g + 2) * kPPitch + pslot] = uint16_t(p23);
       pt[(4 * g + 3) * kPPitch + pslot] = uint16_t(p23 >> 16);
     }
+    // (skipped when no row maximum of this wave's rows moved: alpha is then 1)
+    if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
+        for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
+    }
     __syncthreads();
     // 4. O[:, 128w + 16ct + j] += P . V over the tile's two 32-token blocks.
     //    B fragment of lane (j, g): V[token 32kb2 + 8g + e][128w + 16ct + j],
@@ -294,31 +319,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[w][4 * g + r] = lsum[r];
   }
-  __syncthreads();
+  __syncthreads(); // also: every wave is done with the last tile
+  // Normalized rows through LDS (wave w's 16 x 128 block, fp32, row pitch
+  // 132), so that the stores are 16 bytes per lane.
+  constexpr int kOPitch = 128 + 4;
+  float* ob = reinterpret_cast<float*>(kvt) + w * 16 * kOPitch;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g + r;
-    if (h >= H) continue;
     const float l = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
-    const float lse = (m_run[r] + __builtin_amdgcn_logf(l)) * kLn2;
     const float inv = 1.0f / l; // one division per row; the outputs take a product
-    if constexpr (PD == kDirect) {
-      uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent + 128 * w + j;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = uint16_t(bf16x2_rne(acc[ct][r] * inv, 0.f));
-      if (a.lse && w == 0 && j == 0) a.lse[size_t(m) * H + h] = lse;
-    } else {
-      const size_t prow = (size_t(m) * S + s) * H + h;
-      if constexpr (PD == kPartialFp32) {
-        float* orow = static_cast<float*>(a.part) + prow * kLatent + 128 * w + j;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = acc[ct][r] * inv;
+    for (int ct = 0; ct < 8; ++ct) ob[h * kOPitch + 16 * ct + j] = acc[ct][r] * inv;
+    if (w == 0 && j == 0 && h < H) {
+      const float lse = (m_run[r] + __builtin_amdgcn_logf(l)) * kLn2;
+      if constexpr (PD == kDirect) {
+        if (a.lse) a.lse[size_t(m) * H + h] = lse;
       } else {
-        uint16_t* orow = static_cast<uint16_t*>(a.part) + prow * kLatent + 128 * w + j;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) orow[16 * ct] = uint16_t(bf16x2_rne(acc[ct][r] * inv, 0.f));
+        a.part_lse[(size_t(m) * S + s) * H + h] = lse;
       }
-      if (w == 0 && j == 0) a.part_lse[prow] = lse;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Lane (row = lane / 4, quarter = lane % 4) of each of four passes writes 8
+  // consecutive columns (16 bytes of bf16, 32 of fp32) of one row.
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int h = lane >> 2, c8 = 8 * (4 * pass + (lane & 3)); // column within the wave's 128
+    if (h >= H) continue;
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(ob + h * kOPitch + c8);
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(ob + h * kOPitch + c8 + 4);
+    const int col = 128 * w + c8;
+    if constexpr (PD == kPartialFp32) {
+      float* dst = static_cast<float*>(a.part) + ((size_t(m) * S + s) * H + h) * kLatent + col;
+      *reinterpret_cast<f32x4_t*>(dst) = x0;
+      *reinterpret_cast<f32x4_t*>(dst + 4) = x1;
+    } else {
+      uint16_t* dst = PD == kDirect ? a.out + (size_t(m) * H + h) * kLatent + col
+                                    : static_cast<uint16_t*>(a.part) + ((size_t(m) * S + s) * H + h) * kLatent + col;
+      *reinterpret_cast<u32x4_t*>(dst) =
+          u32x4_t{bf16x2_rne(x0[0], x0[1]), bf16x2_rne(x0[2], x0[3]), bf16x2_rne(x1[0], x1[1]), bf16x2_rne(x1[2], x1[3])};
     }
   }
 }
