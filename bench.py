@@ -29,6 +29,8 @@ Printed JSON line (stdout, one line):
   attention   dense MLA decode attention with BF16 / FP32 split partials over
               a cold paged cache: 32 x 4096 tokens and 1 x 65536 tokens,
               H=16, us per call and GB/s against the HBM peak
+  decode_layer the three kernels chained as one MLA decode layer (query,
+              attention, V up-projection) in a hipGraph, us per layer
   staged      the staged path (torch.bmm + copies + E4M3 quantization) of the
               same step on the same GPU
   cpu_baseline the CPU oracle timed on this host over a bounded sample of the
@@ -71,6 +73,7 @@ def parse():
     p.add_argument("--no-pages-shape", action="store_true")
     p.add_argument("--no-uv", action="store_true")
     p.add_argument("--no-attention", action="store_true")
+    p.add_argument("--no-layer", action="store_true")
     p.add_argument("--attention-only", action="store_true",
                    help="run only the attention leg and print its JSON (for profiling; no bench line)")
     p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
@@ -530,6 +533,62 @@ def attention_leg(torch, mq, wl, args):
     return res
 
 
+def layer_leg(torch, mq, wl, args):
+    """One MLA decode layer as the three kernels chain in a hipGraph: the fused
+    query (MXFP8 W_UK_T, BF16 output), dense MLA attention over the decode
+    batch's cold paged cache (32 sequences x 4096 tokens, H=16, BF16 partials,
+    the library's split count) and the V up-projection (MXFP8 W_UV). Four
+    layers, each with its own weights and cache copy, per graph."""
+    M, T, copies = 32, 4096, 4
+    inp = wl.make_attn_inputs(9000, H, [T] * M)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    kv_host = torch.from_numpy(inp.kv.view(np.int16)).view(torch.bfloat16)
+    S = mq.mlaq_attn_num_splits(M, T)
+    pd = mq.MLAQ_PARTIAL_BF16
+    layers = []
+    for l in range(copies):
+        qin = wl.make_inputs(9300 + l, H=H, weight_format=mq.MLAQ_WEIGHT_MXFP8, M_draw=M)
+        rng = np.random.Generator(np.random.PCG64(9400 + l))
+        wuv = wl.e4m3_bits(rng.standard_normal((H, 128, 512), dtype=np.float32) * np.float32(512 ** -0.5))
+        suv = (127 + rng.integers(-8, 1, size=(H, 128, 16))).astype(np.uint8)
+        layers.append({
+            "q_nope": dev_bf16(torch, qin.q_nope), "q_pe": dev_bf16(torch, qin.q_pe), "w": dev_u8(torch, qin.w),
+            "ws": dev_u8(torch, qin.w_scales), "kv": kv_host.cuda(), "wuv": dev_u8(torch, wuv), "suv": dev_u8(torch, suv),
+            "q": torch.empty((M, H, mq.ROW), dtype=torch.bfloat16, device="cuda"),
+            "x": torch.empty((M, H, 512), dtype=torch.bfloat16, device="cuda"),
+            "out": torch.empty((M, H, 128), dtype=torch.bfloat16, device="cuda"),
+            "wsp": torch.empty((mq.mlaq_attn_workspace_size(M, H, S, pd),), dtype=torch.uint8, device="cuda")})
+    del kv_host
+    mq.mlaq_prewarm(H, [M], mq.MLAQ_WEIGHT_MXFP8, mq.MLAQ_OUT_BF16)
+    mq.mlaq_uv_prewarm(H, [M], mq.MLAQ_WEIGHT_MXFP8)
+    mq.mlaq_attn_prewarm(pd)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+            for d in layers:
+                mq.mlaq_run(d["q_nope"], d["q_pe"], d["w"], d["ws"], None, d["q"], mq.MLAQ_WEIGHT_MXFP8,
+                            mq.MLAQ_OUT_BF16)
+                mq.mlaq_attn_run(d["q"], d["kv"], bt, sl, d["x"], inp.softmax_scale, S, pd, d["wsp"])
+                mq.mlaq_uv_run(d["x"], d["wuv"], d["suv"], d["out"], mq.MLAQ_WEIGHT_MXFP8)
+    torch.cuda.synchronize()
+    us = time_graphs(torch, [g], max(4, args.steps // 2), max(2, args.warmup // 2), per_step_units=copies) * 1e3
+    nbytes = (wl.algorithmic_bytes(M, H, mq.MLAQ_WEIGHT_MXFP8, mq.MLAQ_OUT_BF16) + wl.attn_algorithmic_bytes(inp.seq_lens, H)
+              + H * 128 * 512 + H * 128 * 16 + M * H * 512 * 2 + M * H * 128 * 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] MLA decode layer (query + attention + UV, M=32 x 4096 tokens, H=16, MXFP8 weights): "
+        f"{us:.2f} us/layer, {gbs:.1f} GB/s")
+    del g, layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": "MLA decode layer: fused query (MXFP8 W_UK_T, BF16 out) + dense MLA attention (32 sequences "
+                        "x 4096 cached tokens, BF16 partials) + V up-projection (MXFP8 W_UV), H=16, one hipGraph, "
+                        "4 layers with their own weights and cache copies (cold)",
+            "us_per_layer": round(us, 3), "gbs": round(gbs, 1), "bytes_per_layer": nbytes, "num_splits": S}
+
+
 def cpu_baseline_leg(wl, layers, budget_s):
     """The CPU oracle on the step's layers, cycling through them until the
     time budget is spent (the oracle as it stands, threaded over heads)."""
@@ -632,6 +691,7 @@ def main():
     pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
     uv = None if args.no_uv else uv_leg(torch, mq, wl, args)
     attn = None if args.no_attention else attention_leg(torch, mq, wl, args)
+    layer = None if args.no_layer else layer_leg(torch, mq, wl, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
@@ -667,6 +727,7 @@ def main():
         "pages_shape": pages,
         "uv_projection": uv,
         "attention": attn,
+        "decode_layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

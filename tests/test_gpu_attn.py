@@ -28,24 +28,11 @@ import torch
 
 import mla_decode_query_amd as mq
 import oracle
-from gpu_util import dev_bf16, out_bits, ulp_bf16
+from gpu_util import (BF16P, FP32P, assert_attn_parity, attn_oracle_run as oracle_run, dev_bf16, out_bits,
+                      read_partials, ulp_bf16)
 from workloads import make_attn_inputs
 
 pytestmark = pytest.mark.gpu
-
-BF16P, FP32P = mq.MLAQ_PARTIAL_BF16, mq.MLAQ_PARTIAL_FP32
-U = 2.0 ** -24
-
-
-def gamma(n):
-    return n * U / (1 - n * U)
-
-
-def ulp_f32(x):
-    ax = np.abs(np.asarray(x, np.float64))
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    return np.ldexp(1.0, (np.maximum(e, -126) - 23).astype(np.int64))
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _device():
@@ -76,77 +63,6 @@ def run_attn(d, scale, S, pd, q=None, with_ws=False):
     torch.cuda.synchronize()
     res = (out_bits(out), lse.cpu().numpy().astype(np.float64))
     return res + (ws,) if with_ws else res
-
-
-def read_partials(ws, M, H, S, pd):
-    """Partials [M,S,H,512] and lse_s [M,S,H] from the documented workspace layout."""
-    esz = 4 if pd == FP32P else 2
-    nb = M * S * H * 512 * esz
-    raw = ws.cpu().numpy()
-    with np.errstate(invalid="ignore"):  # ranges with no tokens leave their partials unwritten
-        return _decode_partials(raw, nb, M, H, S, pd)
-
-
-def _decode_partials(raw, nb, M, H, S, pd):
-    if pd == FP32P:
-        part = raw[:nb].view(np.float32).astype(np.float64)
-    else:
-        part = oracle.bf16_to_f32(raw[:nb].view(np.uint16)).astype(np.float64)
-    off = (nb + 255) // 256 * 256
-    plse = raw[off:off + M * S * H * 4].view(np.float32).astype(np.float64)
-    return part.reshape(M, S, H, 512), plse.reshape(M, S, H)
-
-
-def oracle_run(inp, S, pd):
-    return oracle.attention(inp.q, inp.kv, inp.block_table, inp.seq_lens, softmax_scale=inp.softmax_scale,
-                            num_splits=S, partial_dtype=pd, threads=16)
-
-
-def _terms(inp, ref):
-    T = inp.seq_lens.astype(np.float64)
-    tprime = T + 2 * 64 + 8
-    gT = np.array([gamma(t) for t in tprime])[:, None]
-    eps = 2 * (gamma(576) + 2.0 ** -22) * ref["smag"] + 2.0 ** -21  # [M,H]
-    vmax = float(np.max(np.abs(oracle.bf16_to_f32(inp.kv[..., :512]))))
-    return gT, eps, vmax
-
-
-def assert_attn_parity(gpu, gpu_lse, ref, inp, S, pd, what, ws=None):
-    gT, eps, vmax = _terms(inp, ref)
-    o = ref["o"]
-    got = oracle.bf16_to_f32(gpu).astype(np.float64)
-    live = inp.seq_lens > 0
-    upart = np.zeros_like(o)
-    lse_mag = np.abs(np.where(np.isfinite(ref["lse"]), ref["lse"], 0.0))
-    if S > 1:
-        ok = np.isfinite(ref["plse"])[..., None]
-        ustore = ulp_bf16(ref["part"]) if pd == BF16P else ulp_f32(ref["part"])
-        upart = np.max(np.where(ok, ustore, 0.0), axis=1)
-        lse_mag = np.maximum(lse_mag, np.max(np.abs(np.where(np.isfinite(ref["plse"]), ref["plse"], 0.0)), axis=1))
-    dlse = 2.0 ** -20 * (1 + lse_mag) + 2 * gT + eps  # [M,H]
-    bound = (ulp_bf16(o) + upart + (2.0 ** -8 + 4 * eps[..., None] + 4 * gT[..., None]) * ref["vabs"]
-             + 4 * dlse[..., None] * vmax + 2.0 ** -20 * np.max(np.abs(o)))
-    bad = ~(np.abs(got - o) <= bound)
-    assert not bad.any(), (f"{what}: {int(bad.sum())} outputs outside the bound, first {np.argwhere(bad)[0]}: "
-                           f"gpu {got[bad][0]} oracle {o[bad][0]} bound {bound[bad][0]}")
-    if live.any():
-        rel = np.linalg.norm(got[live] - o[live]) / max(np.linalg.norm(o[live]), 1e-30)
-        assert rel <= 4e-3, f"{what}: rel-L2 {rel}"
-    # empty sequences: zeros and lse = -inf
-    assert np.all(gpu[~live] == 0), f"{what}: empty sequences must give 0"
-    assert np.all(np.isneginf(gpu_lse[~live])), f"{what}: empty sequences must give lse = -inf"
-    lerr = np.abs(gpu_lse[live] - ref["lse"][live])
-    assert np.all(lerr <= dlse[live]), f"{what}: lse off by {lerr.max()}"
-    if ws is not None and S > 1:
-        part, plse = read_partials(ws, inp.M, inp.H, S, pd)
-        ok = np.isfinite(ref["plse"])
-        assert np.array_equal(np.isneginf(plse), ~ok), f"{what}: empty ranges must store lse = -inf"
-        ustore = ulp_bf16(ref["part"]) if pd == BF16P else ulp_f32(ref["part"])
-        pb = ustore + (2.0 ** -8 + 4 * eps[:, None, :, None] + 4 * gT[:, :, None, None]) * ref["pvabs"]
-        pbad = ok[..., None] & ~(np.abs(part - ref["part"]) <= pb)
-        assert not pbad.any(), f"{what}: {int(pbad.sum())} partials outside the bound, first {np.argwhere(pbad)[0]}"
-        lb = 2.0 ** -20 * (1 + np.abs(np.where(ok, ref["plse"], 0))) + 2 * gT[:, :, None] + eps[:, None, :]
-        assert np.all(np.abs(plse[ok] - ref["plse"][ok]) <= lb[ok]), f"{what}: lse_s"
 
 
 _cache = {}

@@ -11,13 +11,10 @@ import torch
 
 import mla_decode_query_amd as mq
 import oracle
-from gpu_util import dev_bf16, dev_u8, out_bits, ulp_bf16
+from gpu_util import assert_uv_parity, dev_bf16, dev_u8, out_bits
 from workloads import WEIGHT_BF16, WEIGHT_MXFP8, bf16_bits, e4m3_bits
 
 pytestmark = pytest.mark.gpu
-
-GAMMA_512 = (512 * 2.0 ** -24) / (1 - 512 * 2.0 ** -24)
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _device():
@@ -49,16 +46,6 @@ def run_uv(x, w, s, wf, out=None):
     mq.mlaq_uv_run(xd, wd, sd, out, wf)
     torch.cuda.synchronize()
     return out_bits(out)
-
-
-def assert_uv_parity(gpu, ref, what=""):
-    got = oracle.bf16_to_f32(gpu).astype(np.float64)
-    acc = ref["acc"].astype(np.float64)
-    bound = 2 * ulp_bf16(acc) + 2 * GAMMA_512 * ref["s_abs"]
-    bad = ~(np.abs(got - acc) <= bound)
-    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside the bound, first {np.argwhere(bad)[0]}"
-    rel = np.linalg.norm(got - acc) / np.linalg.norm(acc)
-    assert rel <= 4e-3, f"{what}: rel-L2 {rel}"
 
 
 _cache = {}
