@@ -274,3 +274,14 @@ def test_attn_can_implement_and_split_heuristic():
     assert mq.mlaq_attn_num_splits(1, 65536) == min(2 * cus, 256)
     assert mq.mlaq_attn_num_splits(4 * cus, 65536) == 1
     assert mq.mlaq_attn_num_splits(32, 10) == 1
+
+
+def test_attn_many_short_sequences():
+    """1024 sequences of 0..200 tokens (grid and merge grid at scale)."""
+    H = 16
+    lens = [int(x) for x in np.random.Generator(np.random.PCG64(8950)).integers(0, 201, 1024)]
+    inp = make_attn_inputs(8951, H, lens)
+    d = Dev(inp)
+    for S, pd in ((1, BF16P), (3, FP32P)):
+        gpu, lse = run_attn(d, inp.softmax_scale, S, pd)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"1024 sequences S={S}")
