@@ -87,6 +87,8 @@ constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each 16
+constexpr int kRowRor4 = 0x124;       // lane i <- lane (i+4) mod 16
+constexpr int kRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16
 
 // Max / sum over the 16 lanes of a DPP row; every lane gets the result.
 __device__ __forceinline__ float row16_max(float v) {
@@ -100,6 +102,24 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<kQuadXor2>(v);
   v += dpp<kRowHalfMirror>(v);
   return v + dpp<kRowMirror>(v);
+}
+
+// Maxima of four rows over the 16 lanes of a DPP row, transposed: lane j
+// returns the maximum of row 2*(j&1) + ((j>>1)&1) of (v0, v1, v2, v3). The
+// xor-1 partners swap halves (each keeps two rows), the xor-2 partners swap
+// quarters (each keeps one), then two rotations cover all 16 lanes: 5 DPP
+// moves instead of 16 for four separate reductions.
+__device__ __forceinline__ float rows4_max_transposed(float v0, float v1, float v2, float v3, int j) {
+  const bool b0 = j & 1, b1 = (j >> 1) & 1;
+  float k0 = b0 ? v2 : v0, k1 = b0 ? v3 : v1;
+  const float s0 = b0 ? v0 : v2, s1 = b0 ? v1 : v3;
+  k0 = __builtin_fmaxf(k0, dpp<kQuadXor1>(s0));
+  k1 = __builtin_fmaxf(k1, dpp<kQuadXor1>(s1));
+  float k = b1 ? k1 : k0;
+  const float sx = b1 ? k0 : k1;
+  k = __builtin_fmaxf(k, dpp<kQuadXor2>(sx));
+  k = __builtin_fmaxf(k, dpp<kRowRor4>(k));
+  return __builtin_fmaxf(k, dpp<kRowRor8>(k));
 }
 
 // Token range [a, b) of split s of a sequence of T tokens.
@@ -245,15 +265,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     }
     // 2. Masked scores in the log2 domain; tile max per row.
     const bool valid = t0 + trow < tb;
-    float sc[4], mx[4];
+    float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = valid ? sacc[r] * sl2 : -INFINITY;
-      mx[r] = row16_max(sc[r]);
-    }
-    if (j == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[w][4 * g + r] = mx[r];
+    for (int r = 0; r < 4; ++r) sc[r] = valid ? sacc[r] * sl2 : -INFINITY;
+    {
+      const float mx = rows4_max_transposed(sc[0], sc[1], sc[2], sc[3], j);
+      if (j < 4) red[w][4 * g + 2 * (j & 1) + ((j >> 1) & 1)] = mx;
     }
     __syncthreads();
     float alpha[4];

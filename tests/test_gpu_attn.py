@@ -285,3 +285,25 @@ def test_attn_many_short_sequences():
     for S, pd in ((1, BF16P), (3, FP32P)):
         gpu, lse = run_attn(d, inp.softmax_scale, S, pd)
         assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"1024 sequences S={S}")
+
+
+def test_attn_bad_device_values_give_clamped_results():
+    """Negative lengths act as 0 (zeros, lse = -inf); live block-table entries
+    below 0 or past the pool read page 0 or the last page, exactly as the
+    oracle does on the clamped table."""
+    H = 8
+    inp = make_attn_inputs(8960, H, [150, 90, 40])
+    n_pages = inp.kv.shape[0]
+    table = inp.block_table.copy()
+    table[0, 1] = -7
+    table[1, 0] = n_pages + 5
+    sl = inp.seq_lens.copy()
+    sl[2] = -5
+    d = Dev(inp, table=table)
+    d.sl = torch.from_numpy(sl).cuda()
+    got, lse = run_attn(d, inp.softmax_scale, 2, BF16P)
+    clamped = make_attn_inputs(8960, H, [150, 90, 40])
+    clamped.block_table = np.clip(table, 0, n_pages - 1).astype(np.int32)
+    clamped.block_table[2] = -1
+    clamped.seq_lens = np.array([150, 90, 0], np.int32)
+    assert_attn_parity(got, lse, oracle_run(clamped, 2, BF16P), clamped, 2, BF16P, "clamped table")
