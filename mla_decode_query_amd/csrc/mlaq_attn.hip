@@ -25,14 +25,14 @@
 // never stored). Tokens go in 64-token tiles:
 //  - lane (j, g) of wave w loads token 16w + j of a tile: 16 bytes at byte
 //    offset 16(4kb + g) of its 1152-byte row for kb = 0..17, i.e. 64
-//    contiguous bytes of each of 16 rows per instruction; at the start of an
-//    iteration those registers are written row-major into the LDS tile and
-//    the next tile's loads are issued into them, so every tile has a whole
-//    iteration of compute to arrive; its page indices are fetched one tile
-//    earlier still;
+//    contiguous bytes of each of 16 rows per instruction;
 //  - scores: the B fragment of K^T for lane (j, g) is exactly that 16-byte
-//    chunk (8 consecutive dims of token j), so S[h, token] is 18 MFMAs with Q
-//    held in registers as A fragments;
+//    chunk (8 consecutive dims of token j), so S[h, token] is 18 MFMAs
+//    straight from the loaded registers, with Q held in registers as A
+//    fragments; then the value part of the row (its first 1024 bytes) is
+//    written row-major into the LDS tile and the next tile's loads are issued
+//    into the same registers, so every tile has a whole iteration of compute
+//    to arrive; its page indices are fetched one tile earlier still;
 //  - online softmax in the log2 domain: the row max over the tile is reduced
 //    across the 16 lanes of a row with DPP and across the 4 waves through
 //    LDS; the running sums stay per lane until the end;
@@ -183,10 +183,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb) r[kb] = *reinterpret_cast<const u32x4_t*>(rp + 64 * kb);
   };
+  // Only the value part (the first 512 entries) of a row goes to LDS.
   auto stage_tile = [&](const u32x4_t (&r)[kKb]) {
     uint8_t* dst = kvt + trow * kKPitch + 16 * g;
 #pragma unroll
-    for (int kb = 0; kb < kKb; ++kb) *reinterpret_cast<u32x4_t*>(dst + 64 * kb) = r[kb];
+    for (int kb = 0; kb < kVb; ++kb) *reinterpret_cast<u32x4_t*>(dst + 64 * kb) = r[kb];
   };
 
   // Q rows (16 heads, missing ones repeating head H-1) are read from memory
@@ -241,29 +242,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 
   for (int t0 = ta; t0 < tb; t0 += kAttnTile) {
     const uint8_t* tile = kvt;
-    // 0. Stage this tile (its loads had the whole previous iteration to
-    //    arrive) and start the loads of the next one.
+    // 1. Scores S[h = 4g + r, token 16w + j] straight from this lane's
+    //    registers (its token's row, loaded during the previous iteration):
+    //    the B fragment needs no LDS round trip.
+    f32x4_t sacc;
+    {
+      // Two independent accumulator chains (even and odd k-blocks), summed
+      // at the end, so consecutive MFMAs do not wait on each other.
+      f32x4_t s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+        s2[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[kb]),
+                                                             __builtin_bit_cast(bf16x8_t, kr[kb]), s2[kb & 1], 0, 0, 0);
+      sacc = s2[0] + s2[1];
+    }
+    // 2. Stage the value part for the product below (visible after the next
+    //    barrier) and start the loads of the next tile into the same registers.
     stage_tile(kr);
     if (t0 + kAttnTile < tb) {
       load_tile(t0 + kAttnTile, pg_next, kr);
       pg_next = t0 + 2 * kAttnTile < tb ? page_of(t0 + 2 * kAttnTile) : 0;
     }
-    __syncthreads();
-    // 1. Scores S[h = 4g + r, token 16w + j] from the LDS tile.
-    f32x4_t sacc;
-    {
-      // Two independent accumulator chains (even and odd k-blocks), summed
-      // at the end, so consecutive MFMAs do not wait on each other.
-      const uint8_t* krow = tile + trow * kKPitch + 16 * g;
-      f32x4_t s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-        s2[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, qa[kb]),
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 64 * kb)), s2[kb & 1], 0, 0, 0);
-      sacc = s2[0] + s2[1];
-    }
-    // 2. Masked scores in the log2 domain; tile max per row.
+    // 3. Masked scores in the log2 domain; tile max per row.
     const bool valid = t0 + trow < tb;
     float sc[4];
 #pragma unroll
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       const float mx = rows4_max_transposed(sc[0], sc[1], sc[2], sc[3], j);
       if (j < 4) red[w][4 * g + 2 * (j & 1) + ((j >> 1) & 1)] = mx;
     }
-    __syncthreads();
+    __syncthreads(); // also publishes the staged tile
     float alpha[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       l_run[r] = l_run[r] * alpha[r] + p;
       sc[r] = p;
     }
-    // 3. P (bf16) into LDS in slot order; rescale the output accumulators.
+    // 4. P (bf16) into LDS in slot order; rescale the output accumulators.
     {
       const uint32_t p01 = bf16x2_rne(sc[0], sc[1]), p23 = bf16x2_rne(sc[2], sc[3]);
       pt[(4 * g + 0) * kPPitch + pslot] = uint16_t(p01);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
         for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
     }
     __syncthreads();
-    // 4. O[:, 128w + 16ct + j] += P . V over the tile's two 32-token blocks.
+    // 5. O[:, 128w + 16ct + j] += P . V over the tile's two 32-token blocks.
     //    B fragment of lane (j, g): V[token 32kb2 + 8g + e][128w + 16ct + j],
     //    e = 0..7, as two LDS transpose reads (ds_read_b64_tr_b16): within a
     //    16-lane group, output lane i gets element i%4 of the 8 bytes that
