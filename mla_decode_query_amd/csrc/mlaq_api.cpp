@@ -417,13 +417,17 @@ int mlaq_attn_prewarm(int partial_dtype, int device) {
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
   if (e == hipSuccess && cur != device) e = hipSetDevice(device);
-  const void* fns[] = {mlaq::attn_split_kernel_for(partial_dtype, false), mlaq::attn_split_kernel_for(partial_dtype, true),
-                       mlaq::attn_merge_kernel_for(partial_dtype, 2),
-                       mlaq::attn_merge_kernel_for(partial_dtype, mlaq::kAttnMaxSplits)};
-  for (const void* fn : fns) {
+  const void* split[] = {mlaq::attn_split_kernel_for(partial_dtype, false),
+                         mlaq::attn_split_kernel_for(partial_dtype, true)};
+  for (const void* fn : split) {
     hipFuncAttributes attr;
     if (e == hipSuccess) e = hipFuncGetAttributes(&attr, fn);
   }
+  for (int parts = 1; parts <= 16; parts *= 2)
+    for (int r = 1; r <= 8; r *= 2) {
+      hipFuncAttributes attr;
+      if (e == hipSuccess) e = hipFuncGetAttributes(&attr, mlaq::attn_merge_kernel_for(partial_dtype, parts, r));
+    }
   if (cur != device) (void)hipSetDevice(cur);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading attention kernels: %s", hipGetErrorString(e));
   return MLAQ_OK;
@@ -512,9 +516,12 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   void* kargs[] = {&ka};
   const hipStream_t st_ = static_cast<hipStream_t>(stream);
   const bool direct = a.num_splits == 1;
+  int parts = 1, per_thread = 1;
+  mlaq::attn_merge_shape(a.M, a.H, a.num_splits, &parts, &per_thread);
   e = hipLaunchKernel(mlaq::attn_split_kernel_for(a.partial_dtype, direct), split_grid, block, kargs, 0, st_);
   if (e == hipSuccess && !direct)
-    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype, a.num_splits), merge_grid, block, kargs, 0, st_);
+    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype, parts, per_thread), merge_grid, block, kargs, 0,
+                        st_);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;
 }

@@ -69,6 +69,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPartialBf16 = MLAQ_PARTIAL_BF16;
 constexpr int kPartialFp32 = MLAQ_PARTIAL_FP32;
 constexpr int kDirect = 2; // one split: write the final output
+constexpr int kMergeMaxR = 8;  // most ranges per merge thread (all requested at once)
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -402,72 +403,79 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v + lane_value(v, lane ^ 32);
 }
 
-// Merge: one workgroup per (m, h, column part): QN parts of 512/QN columns
-// (QN = 4 from 32 ranges on, else 1). Thread t takes 8 columns (t % CG)
-// and the ranges s = t/CG + RG k. Every wave first requests the lse values,
-// then its first partials, and forms L = max_s lse_s and the weights
-// exp(lse_s - L) on its own (no workgroup barrier); the RG range groups'
-// sums are added in order at the end.
-template <int PD, int QN>
+// Merge: one workgroup per (m, h, column part), QN parts of 512/QN columns.
+// Thread t takes 8 columns (t % CG) of the ranges s = t/CG + RG u,
+// u = 0..R-1, with RG = 4 QN range groups and R >= S / RG chosen by the host,
+// so every partial a thread reads is requested at once, together with the
+// lse values, with no branch between the loads. Each wave forms L = max_s lse_s and the weights
+// exp(lse_s - L) on its own (no workgroup barrier). The range groups' sums
+// are then added in a fixed order: four per thread into QN slices, then the
+// QN slices (deterministic, no atomics).
+template <int PD, int QN, int R>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
-  constexpr int kMergeCols = kLatent / QN;                 // columns per workgroup
-  constexpr int CG = kMergeCols / 8;                       // column groups (8 columns each)
-  constexpr int RG = kAttnThreads / CG;                    // range groups
-  __shared__ float wts[4][kAttnMaxSplits];                 // each wave's copy of the weights
-  __shared__ __attribute__((aligned(16))) float part_sum[RG][kMergeCols];
-  constexpr int kFirst = 4;                                // ranges per thread requested up front
+  constexpr int kCols = kLatent / QN;         // columns per workgroup
+  constexpr int CG = kCols / 8;               // column groups (8 columns each)
+  constexpr int RG = kAttnThreads / CG;       // range groups (4 QN)
+  constexpr int kPairs = kCols / 2;           // column pairs
+  constexpr int KS = kAttnThreads / kPairs;   // slices of the range groups (QN)
+  constexpr int RPS = RG / KS;                // range groups per slice (4)
+  static_assert(RG == 4 * QN && KS == QN && RPS == 4, "merge shape");
+  static_assert(R >= 1 && R <= kMergeMaxR, "ranges per thread");
+  constexpr int kLv = (RG * R + 63) / 64; // lse values per lane (S <= RG R)
+  static_assert(kAttnMaxSplits <= 4 * 16 * kMergeMaxR, "every split count has a shape");
+  __shared__ float wts[4][kAttnMaxSplits];    // each wave's copy of the weights
+  __shared__ __attribute__((aligned(16))) float part_sum[RG][kCols];
+  __shared__ __attribute__((aligned(8))) float slice_sum[KS][kCols];
   const int H = a.H, S = a.S;
-  const int mh = blockIdx.x / QN, quarter = blockIdx.x - (blockIdx.x / QN) * QN;
+  const int mh = blockIdx.x / QN, part = blockIdx.x - (blockIdx.x / QN) * QN;
   const int m = mh / H, h = mh - (mh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = tid % CG, rg = tid / CG;
-  const int c = kMergeCols * quarter + 8 * cg;
+  const int c = kCols * part + 8 * cg;
   const size_t stride = size_t(H) * kLatent; // elements between consecutive ranges
   const size_t base = (size_t(m) * S * H + h) * kLatent + c;
 
-  // 1. lse values (lane l holds s = l + 64i), then this thread's first
-  //    ranges, all in flight before any wait.
+  // 1. lse values (lane l holds s = l + 64i), then this thread's ranges, all
+  //    requested before any wait (the loads take no branch: an index past
+  //    S re-reads range S-1 and is replaced by -inf once loaded).
   const float* pl = a.part_lse + size_t(m) * S * H + h;
-  float lv[kAttnMaxSplits / 64];
+  float lv[kLv];
 #pragma unroll
-  for (int i = 0; i < kAttnMaxSplits / 64; ++i) {
+  for (int i = 0; i < kLv; ++i) {
     const int s = lane + 64 * i;
-    lv[i] = s < S ? pl[size_t(s) * H] : -INFINITY;
+    lv[i] = pl[size_t(s < S ? s : S - 1) * H];
   }
-  f32x4_t v[kFirst][2];
-  auto load_range = [&](int s, f32x4_t (&dst)[2]) {
-    const size_t off = base + size_t(s < S ? s : 0) * stride; // past S: range 0, weight 0
+  // Raw partials (8 bf16 in 16 bytes, or 8 fp32 in 32). A slot past this
+  // thread's last range re-reads range S-1 (a line other threads read
+  // anyway) and is never added.
+  typedef u32x4_t raw_t[PD == kPartialFp32 ? 2 : 1];
+  raw_t v[R];
+  auto load_range = [&](int s, raw_t& dst) {
+    const size_t off = base + size_t(s < S ? s : S - 1) * stride;
     if constexpr (PD == kPartialFp32) {
-      dst[0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off);
-      dst[1] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part) + off + 4);
+      dst[0] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a.part) + off);
+      dst[1] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a.part) + off + 4);
     } else {
-      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part) + off);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        dst[i][0] = __uint_as_float(b[2 * i] << 16);
-        dst[i][1] = __uint_as_float(b[2 * i] & 0xFFFF0000u);
-        dst[i][2] = __uint_as_float(b[2 * i + 1] << 16);
-        dst[i][3] = __uint_as_float(b[2 * i + 1] & 0xFFFF0000u);
-      }
+      dst[0] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part) + off);
     }
   };
+  const int nr = rg < S ? (S - rg + RG - 1) / RG : 0; // this thread's ranges
 #pragma unroll
-  for (int u = 0; u < kFirst; ++u) load_range(rg + RG * u, v[u]);
+  for (int u = 0; u < R; ++u) load_range(rg + RG * u, v[u]);
 
   // 2. L and the weights, per wave.
+#pragma unroll
+  for (int i = 0; i < kLv; ++i)
+    if (lane + 64 * i >= S) lv[i] = -INFINITY;
   float L = lv[0];
 #pragma unroll
-  for (int i = 1; i < kAttnMaxSplits / 64; ++i) L = __builtin_fmaxf(L, lv[i]);
+  for (int i = 1; i < kLv; ++i) L = __builtin_fmaxf(L, lv[i]);
   L = wave_max(L);
   uint16_t* orow = a.out + (size_t(m) * H + h) * kLatent;
-  if (L == -INFINITY) { // no tokens at all
-    if (rg == 0) *reinterpret_cast<u32x4_t*>(orow + c) = u32x4_t{0u, 0u, 0u, 0u};
-    if (a.lse && quarter == 0 && tid == 0) a.lse[size_t(m) * H + h] = -INFINITY;
-    return;
-  }
+  // (L = -inf: no tokens at all; every weight is 0 and so is the output.)
   float wsum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kAttnMaxSplits / 64; ++i) {
+  for (int i = 0; i < kLv; ++i) {
     const int s = lane + 64 * i;
     const float wt = lv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lv[i] - L) * kLog2e);
     if (s < S) wts[w][s] = wt;
@@ -478,41 +486,60 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 3. Weighted sum of this thread's ranges.
+  // 3. Weighted sum of this thread's ranges, in order of s.
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](int s, const f32x4_t (&x)[2]) {
-    if (s >= S) return;
-    const float wt = wts[w][s];
-    if (wt == 0.f) return; // a range without tokens holds no partial
+  // A range without tokens (weight 0) holds no partial: its bytes are not
+  // used. The products are selected rather than branched over, so the loads
+  // above stay ahead of every wait.
+  auto add = [&](int u, const raw_t& x) {
+    const float wt = u < nr ? wts[w][rg + RG * (u < nr ? u : 0)] : 0.f;
+    float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      o[i] += wt * x[0][i];
-      o[4 + i] += wt * x[1][i];
+      if constexpr (PD == kPartialFp32) {
+        f[i] = __uint_as_float(x[0][i]);
+        f[4 + i] = __uint_as_float(x[1][i]);
+      } else {
+        f[2 * i] = __uint_as_float(x[0][i] << 16);
+        f[2 * i + 1] = __uint_as_float(x[0][i] & 0xFFFF0000u);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] += wt != 0.f ? wt * f[i] : 0.f;
   };
 #pragma unroll
-  for (int u = 0; u < kFirst; ++u) add(rg + RG * u, v[u]);
-  for (int s0 = rg + RG * kFirst; s0 < S; s0 += RG * kFirst) {
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u) load_range(s0 + RG * u, v[u]);
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u) add(s0 + RG * u, v[u]);
-  }
+  for (int u = 0; u < R; ++u) add(u, v[u]);
 
-  // 4. The range groups' sums, in order.
+  // 4. The range groups' sums: RPS consecutive groups per slice, then the
+  //    slices, each in order.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part_sum[rg][8 * cg + i] = o[i];
+  for (int i = 0; i < 8; i += 4)
+    *reinterpret_cast<f32x4_t*>(&part_sum[rg][8 * cg + i]) = f32x4_t{o[i], o[i + 1], o[i + 2], o[i + 3]};
   __syncthreads();
-  if (tid < kMergeCols / 2) {
-    float x0 = 0.f, x1 = 0.f;
+  const int pr = tid % kPairs, ks = tid / kPairs;
+  float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-    for (int k = 0; k < RG; ++k) {
-      x0 += part_sum[k][2 * tid];
-      x1 += part_sum[k][2 * tid + 1];
-    }
-    *reinterpret_cast<uint32_t*>(orow + kMergeCols * quarter + 2 * tid) = bf16x2_rne(x0 / wsum, x1 / wsum);
-    if (a.lse && quarter == 0 && tid == 0) a.lse[size_t(m) * H + h] = L + __builtin_amdgcn_logf(wsum) * kLn2;
+  for (int k = 0; k < RPS; ++k) {
+    x0 += part_sum[RPS * ks + k][2 * pr];
+    x1 += part_sum[RPS * ks + k][2 * pr + 1];
   }
+  if constexpr (KS > 1) {
+    slice_sum[ks][2 * pr] = x0;
+    slice_sum[ks][2 * pr + 1] = x1;
+    __syncthreads();
+    if (tid >= kPairs) return;
+    x0 = 0.f;
+    x1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      x0 += slice_sum[k][2 * pr];
+      x1 += slice_sum[k][2 * pr + 1];
+    }
+  }
+  const bool any = wsum > 0.f;
+  *reinterpret_cast<uint32_t*>(orow + kCols * part + 2 * pr) =
+      bf16x2_rne(any ? x0 / wsum : 0.f, any ? x1 / wsum : 0.f);
+  if (a.lse && part == 0 && tid == 0) a.lse[size_t(m) * H + h] = any ? L + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
 } // namespace
@@ -524,24 +551,55 @@ const void* attn_split_kernel_for(int partial_dtype, bool direct) {
   return nullptr;
 }
 
-// Column parts of the merge for S ranges: four from 32 ranges on (more
-// workgroups, fewer ranges per thread), else one (fewer, fuller workgroups).
-int attn_merge_parts(int S) { return S >= 32 ? 4 : 1; }
+// Merge shape for M rows of H heads and S ranges: QN column parts (RG =
+// 4 QN range groups) and R ranges per thread. QN is the smallest power of two
+// with 4 QN kMergeMaxR >= S, doubled while M H QN workgroups would leave
+// compute units idle (at most 16); R is the smallest power of two covering
+// the ranges of a thread.
+void attn_merge_shape(int M, int H, int S, int* parts, int* per_thread) {
+  int qn = 1;
+  while (qn < 16 && 4 * qn * kMergeMaxR < S) qn *= 2;
+  while (qn < 16 && (long long)M * H * qn < 256) qn *= 2;
+  int r = 1;
+  while (r < kMergeMaxR && 4 * qn * r < S) r *= 2;
+  *parts = qn;
+  *per_thread = r;
+}
 
-const void* attn_merge_kernel_for(int partial_dtype, int S) {
-  const bool q = attn_merge_parts(S) == 4;
-  if (partial_dtype == MLAQ_PARTIAL_FP32)
-    return q ? reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32, 4>)
-             : reinterpret_cast<const void*>(&attn_merge_kernel<kPartialFp32, 1>);
-  if (partial_dtype == MLAQ_PARTIAL_BF16)
-    return q ? reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16, 4>)
-             : reinterpret_cast<const void*>(&attn_merge_kernel<kPartialBf16, 1>);
+template <int PD, int QN>
+const void* merge_kernel_r(int r) {
+  switch (r) {
+  case 1: return reinterpret_cast<const void*>(&attn_merge_kernel<PD, QN, 1>);
+  case 2: return reinterpret_cast<const void*>(&attn_merge_kernel<PD, QN, 2>);
+  case 4: return reinterpret_cast<const void*>(&attn_merge_kernel<PD, QN, 4>);
+  case 8: return reinterpret_cast<const void*>(&attn_merge_kernel<PD, QN, 8>);
+  default: return nullptr;
+  }
+}
+
+template <int PD>
+const void* merge_kernel(int parts, int r) {
+  switch (parts) {
+  case 1: return merge_kernel_r<PD, 1>(r);
+  case 2: return merge_kernel_r<PD, 2>(r);
+  case 4: return merge_kernel_r<PD, 4>(r);
+  case 8: return merge_kernel_r<PD, 8>(r);
+  case 16: return merge_kernel_r<PD, 16>(r);
+  default: return nullptr;
+  }
+}
+
+const void* attn_merge_kernel_for(int partial_dtype, int parts, int per_thread) {
+  if (partial_dtype == MLAQ_PARTIAL_FP32) return merge_kernel<kPartialFp32>(parts, per_thread);
+  if (partial_dtype == MLAQ_PARTIAL_BF16) return merge_kernel<kPartialBf16>(parts, per_thread);
   return nullptr;
 }
 
 void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block) {
   *split_grid = dim3(unsigned(M) * unsigned(S), 1, 1);
-  *merge_grid = dim3(unsigned(M) * unsigned(H) * unsigned(attn_merge_parts(S)), 1, 1);
+  int parts = 1, r = 1;
+  attn_merge_shape(M, H, S, &parts, &r);
+  *merge_grid = dim3(unsigned(M) * unsigned(H) * unsigned(parts), 1, 1);
   *block = dim3(kAttnThreads, 1, 1);
 }
 

@@ -83,7 +83,11 @@ struct AttnArgs {
 // Split kernel (per partial dtype, or the direct one-split form) and merge
 // kernel, and their launch shapes.
 const void* attn_split_kernel_for(int partial_dtype, bool direct);
-const void* attn_merge_kernel_for(int partial_dtype, int num_splits);
+// The merge kernel for a shape (column parts 1, 2, 4, 8 or 16; ranges per
+// thread 1, 2, 4 or 8; null otherwise), and the shape used for M rows of H
+// heads and S ranges.
+const void* attn_merge_kernel_for(int partial_dtype, int parts, int per_thread);
+void attn_merge_shape(int M, int H, int S, int* parts, int* per_thread);
 void attn_launch_shapes(int M, int H, int S, dim3* split_grid, dim3* merge_grid, dim3* block);
 
 // Host function pointer of the kernel for a variant (null if none).
