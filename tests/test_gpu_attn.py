@@ -287,6 +287,32 @@ def test_attn_many_short_sequences():
         assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"1024 sequences S={S}")
 
 
+# (M, H, S) per merge instantiation: the merge kernel takes QN column parts
+# (the smallest power of two with 32 QN >= S, doubled while M H QN < 256, at
+# most 16) and R ranges per thread (the smallest power of two with
+# 4 QN R >= S); these 19 shapes give every reachable (QN, R).
+MERGE_SHAPES = [
+    (16, 16, 3), (16, 16, 7), (16, 16, 16), (16, 16, 32),     # QN 1, R 1/2/4/8
+    (8, 16, 5), (8, 16, 12), (8, 16, 30), (8, 16, 64),        # QN 2
+    (4, 16, 16), (4, 16, 20), (4, 16, 50), (4, 16, 128),      # QN 4
+    (2, 16, 2), (2, 16, 33), (2, 16, 100), (2, 16, 256),      # QN 8
+    (1, 16, 2), (1, 16, 100), (1, 16, 200),                   # QN 16
+]
+
+
+@pytest.mark.parametrize("M,H,S", MERGE_SHAPES)
+def test_attn_merge_shapes(M, H, S):
+    """Every merge instantiation against the oracle's split procedure: ragged
+    lengths near 64 S tokens (most ranges full, the last ones short or
+    empty), BF16 partials, and FP32 partials for the larger split counts."""
+    lens = [max(1, min(64 * S, 6000) - 37 * i) for i in range(M)]
+    inp = cached_inputs(8970 + M + S, H, lens)
+    d = Dev(inp)
+    for pd in ((BF16P, FP32P) if S >= 64 else (BF16P,)):
+        gpu, lse, ws = run_attn(d, inp.softmax_scale, S, pd, with_ws=True)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"merge M={M} H={H} S={S} pd={pd}", ws)
+
+
 def test_attn_bad_device_values_give_clamped_results():
     """Negative lengths act as 0 (zeros, lse = -inf); live block-table entries
     below 0 or past the pool read page 0 or the last page, exactly as the
