@@ -346,10 +346,11 @@ int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* 
   if (st != MLAQ_OK) return st;
   st = mlaq_uv_plan_supported(H, M, MLAQ_LATENT_DIM, MLAQ_V_DIM, weight_format, arch);
   if (st != MLAQ_OK) return st;
-  const void* fn = mlaq::uv_kernel_for(weight_format, M <= 16 ? 1 : 2);
+  const int m_tiles = M <= 16 ? 1 : 2;
+  const void* fn = mlaq::uv_kernel_for(weight_format, m_tiles);
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
-  mlaq::uv_launch_shape(H, &grid, &block);
+  mlaq::uv_launch_shape(H, m_tiles, &grid, &block);
   mlaq::UvArgs ka{static_cast<const uint16_t*>(x), w_uv, static_cast<const uint8_t*>(w_uv_scales), out, M, H};
   void* kargs[] = {&ka};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));

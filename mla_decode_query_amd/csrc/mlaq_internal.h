@@ -56,7 +56,7 @@ struct UvArgs {
 
 // V up-projection kernel for a weight format and M tile count, and its grid.
 const void* uv_kernel_for(int weight_format, int m_tiles);
-void uv_launch_shape(int H, dim3* grid, dim3* block);
+void uv_launch_shape(int H, int m_tiles, dim3* grid, dim3* block);
 
 // Dense MLA decode attention (all tensors contiguous in their inner
 // dimension; q rows strided).

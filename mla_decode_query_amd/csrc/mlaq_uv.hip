@@ -12,11 +12,17 @@
 // memory, so a lane's 16-byte load of 8 consecutive c of one value column is
 // directly its B fragment for v_mfma_f32_16x16x32_bf16 (element e of lane
 // j + 16g = row c0 + 8g + e of column j), and the A fragment is the same
-// 8 c of token j's x row. A workgroup (4 waves) owns one head and CB value
-// columns; wave w reduces c in [128w, 128w+128) over four MFMAs, and the
-// four partial tiles are summed through LDS in a fixed order. With CB = 8 the
-// upper 8 MFMA columns repeat the lower 8 (same addresses, so no extra HBM
-// traffic) and are dropped: 16 workgroups per head, 256 at H = 16.
+// 8 c of token j's x row. A workgroup (4 waves) owns one head, CB value
+// columns and one 16-token tile; wave w reduces c in [128w, 128w+128) over
+// four MFMAs, and the four partial tiles are summed through LDS in a fixed
+// order. Every workgroup reads its head's x rows for its tile from L2, which
+// is the per-CU traffic that grows with M, so the shape keeps 256 workgroups
+// at H = 16 either way: for M <= 16, CB = 8 (the upper 8 MFMA columns repeat
+// the lower 8 at the same addresses, so no extra HBM traffic, and are
+// dropped), 16 workgroups per head; for M <= 32, CB = 16 and the two token
+// tiles in workgroups of their own (8 column blocks x 2 tiles per head), the
+// two tiles of a column block on the same XCD so its weights come from HBM
+// once.
 //
 // MXFP8: a lane loads 8 E4M3 bytes and the one E8M0 byte of their 32-group;
 // v_cvt_pk_f32_fp8 times 2^(S-127) is exact and its top half is the exact
@@ -33,10 +39,10 @@ using namespace dev;
 constexpr int kUvThreads = 256; // 4 waves
 constexpr int kUvScalesPerRow = kLatent / kMxBlock;
 
-template <int WF, int MT, int CB>
+template <int WF, int NMT, int CB>
 __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   constexpr int NVB = kValue / CB; // column blocks per head
-  constexpr int MROWS = 16 * MT;
+  constexpr int MROWS = 16;        // tokens per workgroup
   constexpr int LDW = CB + 4;
   static_assert(CB == 8 || CB == 16, "8 or 16 value columns per workgroup");
   __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
@@ -44,8 +50,11 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
+  // Tile = (head, column block, token tile), the token tile fastest, so the
+  // XCD-contiguous tile ranges keep both token tiles of a block together.
   const int tile = tile_of_block(blockIdx.x, gridDim.x);
-  const int h = tile / NVB, vb = tile - h * NVB;
+  const int h = tile / (NVB * NMT), hr = tile - h * (NVB * NMT);
+  const int vb = hr / NMT, mt = hr - (hr / NMT) * NMT;
   const int v = vb * CB + (j % CB); // this lane's value column
   const int M = a.M, H = a.H;
   const int cbase = 128 * wave + 8 * g; // + 32 kb: this lane's 8 latent values per MFMA
@@ -69,23 +78,20 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
     for (int kb = 0; kb < 4; ++kb) wb[kb] = u32x4_t{w8[kb][0], w8[kb][1], 0u, 0u}; // decoded below
   }
 
-  // 2. A fragments: token 16t + j, the same 8 latent values per k-block.
+  // 2. A fragments: token 16 mt + j, the same 8 latent values per k-block.
   //    Rows past M read token 0; their MFMA output rows are never stored.
-  u32x4_t xa[MT][4];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = 16 * t + j;
+  u32x4_t xa[4];
+  {
+    const int m = 16 * mt + j;
     const int mc = m < M ? m : 0;
     const uint32_t off = ((uint32_t(mc) * H + h) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) xa[t][kb] = *at_byte<const u32x4_t>(a.x, off + 64 * kb);
+    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 64 * kb);
   }
   __builtin_amdgcn_sched_barrier(0); // every load is in flight before any wait
 
   // 3. Contraction over this wave's 128 latent values.
-  f32x4_t acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     u32x4_t b = wb[kb];
@@ -102,27 +108,24 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
       }
       b = d;
     }
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[t][kb]),
-                                                       __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[kb]),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   }
 
-  // 4. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of column j.
+  // 4. Partial tiles to LDS: lane (j, g) holds tokens 16 mt + 4g + r of column j.
   if (j < CB) {
     float* pw = part + wave * MROWS * LDW;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[(16 * t + 4 * g + r) * LDW + j] = acc[t][r];
+    for (int r = 0; r < 4; ++r) pw[(4 * g + r) * LDW + j] = acc[r];
   }
   __syncthreads();
 
   // 5. Epilogue: sum the four partials in order, round, store 4 columns.
   constexpr int GPR = CB / 4;
-  for (int x = tid; x < M * GPR; x += kUvThreads) {
-    const int m = x / GPR, cg = x - m * GPR;
-    const int off = m * LDW + 4 * cg;
+  const int m0 = 16 * mt, rows = M - m0 < MROWS ? M - m0 : MROWS; // tokens of this tile below M
+  for (int x = tid; x < rows * GPR; x += kUvThreads) {
+    const int ml = x / GPR, cg = x - ml * GPR, m = m0 + ml;
+    const int off = ml * LDW + 4 * cg;
     f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
 #pragma unroll
     for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
@@ -131,12 +134,13 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   }
 }
 
-// Value columns per workgroup: 8 (256 workgroups at H = 16).
-constexpr int kUvCols = 8;
+// Value columns per workgroup: 8 with one token tile, 16 with two (256
+// workgroups at H = 16 either way).
+constexpr int uv_cols(int m_tiles) { return m_tiles == 1 ? 8 : 16; }
 
-template <int WF, int MT>
+template <int WF, int NMT>
 const void* uv_kernel_ptr() {
-  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, MT, kUvCols>);
+  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, NMT, uv_cols(NMT)>);
 }
 
 } // namespace
@@ -148,8 +152,8 @@ const void* uv_kernel_for(int weight_format, int m_tiles) {
   return nullptr;
 }
 
-void uv_launch_shape(int H, dim3* grid, dim3* block) {
-  *grid = dim3(unsigned(H * (kValue / kUvCols)), 1, 1);
+void uv_launch_shape(int H, int m_tiles, dim3* grid, dim3* block) {
+  *grid = dim3(unsigned(H * (kValue / uv_cols(m_tiles)) * m_tiles), 1, 1);
   *block = dim3(kUvThreads, 1, 1);
 }
 
