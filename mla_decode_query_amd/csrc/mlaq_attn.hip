@@ -142,7 +142,7 @@ template <int PD>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kvt[kTileBytes]; // the current tile, row = token
   __shared__ __attribute__((aligned(16))) uint16_t pt[16 * kPPitch];  // P tile (bf16), row = head
-  __shared__ float red[4][16];                                         // per-wave row max / sum
+  __shared__ __attribute__((aligned(16))) float red[4][16];            // per-wave row max / sum
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -342,15 +342,31 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   // 132), so that the stores are 16 bytes per lane.
   constexpr int kOPitch = 128 + 4;
   float* ob = reinterpret_cast<float*>(kvt) + w * 16 * kOPitch;
+  // This lane's four rows 4g..4g+3: the waves' sums in order, then one
+  // reciprocal per row (the outputs take a product; l >= 1, since the row
+  // maximum's own weight is 1).
+  float l[4], inv[4];
+  {
+    const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(&red[0][4 * g]);
+    const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(&red[1][4 * g]);
+    const f32x4_t r2 = *reinterpret_cast<const f32x4_t*>(&red[2][4 * g]);
+    const f32x4_t r3 = *reinterpret_cast<const f32x4_t*>(&red[3][4 * g]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * g + r;
-    const float l = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
-    const float inv = 1.0f / l; // one division per row; the outputs take a product
+    for (int r = 0; r < 4; ++r) {
+      l[r] = ((r0[r] + r1[r]) + r2[r]) + r3[r];
+      inv[r] = __builtin_amdgcn_rcpf(l[r]);
+    }
+  }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) ob[h * kOPitch + 16 * ct + j] = acc[ct][r] * inv;
-    if (w == 0 && j == 0 && h < H) {
-      const float lse = (m_run[r] + __builtin_amdgcn_logf(l)) * kLn2;
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) ob[(4 * g + r) * kOPitch + 16 * ct + j] = acc[ct][r] * inv[r];
+  if (w == 0 && j == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;
+      if (h >= H) break;
+      const float lse = (m_run[r] + __builtin_amdgcn_logf(l[r])) * kLn2;
       if constexpr (PD == kDirect) {
         if (a.lse) a.lse[size_t(m) * H + h] = lse;
       } else {
