@@ -377,7 +377,7 @@ int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits) {
   int cus = 0;
   int st = device_cus(device, &cus);
   if (st != MLAQ_OK) return st;
-  // Two split workgroups per compute unit (each holds one 74 KiB LDS tile),
+  // Two split workgroups per compute unit (each holds a 66 KiB LDS tile),
   // ranges of at least 256 tokens (four 64-token tiles).
   long long want = 2LL * cus / M;
   const long long by_len = (max_seq_len + 255) / 256;

@@ -19,7 +19,7 @@
 // on a 64-token tile.
 //
 // Split kernel, one workgroup (4 waves) per (m, s), two workgroups per
-// compute unit (each holds one 74 KiB LDS tile), so one workgroup's compute
+// compute unit (each holds a 66 KiB LDS tile), so one workgroup's compute
 // covers the other's waits. Heads are the 16 rows of
 // v_mfma_f32_16x16x32_bf16 (H <= 16; missing rows repeat head H-1 and are
 // never stored). Tokens go in 64-token tiles:
@@ -60,8 +60,14 @@ using namespace dev;
 constexpr int kAttnThreads = 256;           // 4 waves
 constexpr int kKb = kRow / 32;              // 18 k-blocks of the 576-wide score product
 constexpr int kVb = kLatent / 32;           // the first 16 of them are the value
-constexpr int kKPitch = 2 * kRow + 32;      // bytes per token row of an LDS tile (1184)
-constexpr int kTileBytes = kAttnTile * kKPitch;
+// The LDS tile holds the value part of each token row (1024 bytes) at a
+// 1056-byte pitch: consecutive rows start 8 banks apart, so the 16 lanes of
+// a transpose read (4 rows x 32 bytes) hit 32 different banks. Before the
+// first tile it stages the 16 query rows (1152 bytes each) at their own pitch.
+constexpr int kVPitch = 2 * kLatent + 32;   // 1056
+constexpr int kQPitch = 2 * kRow + 32;      // 1184
+constexpr int kTileBytes = kAttnTile * kVPitch;
+static_assert(16 * kQPitch <= kTileBytes, "query staging fits the tile");
 constexpr int kPPitch = kAttnTile + 8;      // bf16 per head row of the LDS P tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   };
   // Only the value part (the first 512 entries) of a row goes to LDS.
   auto stage_tile = [&](const u32x4_t (&r)[kKb]) {
-    uint8_t* dst = kvt + trow * kKPitch + 16 * g;
+    uint8_t* dst = kvt + trow * kVPitch + 16 * g;
 #pragma unroll
     for (int kb = 0; kb < kVb; ++kb) *reinterpret_cast<u32x4_t*>(dst + 64 * kb) = r[kb];
   };
@@ -218,13 +224,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     const int cidx = tid + kAttnThreads * k;
     if (cidx < kQChunks) {
       const int hh = cidx / (kRow / 8), part = cidx - hh * (kRow / 8);
-      *reinterpret_cast<u32x4_t*>(kvt + hh * kKPitch + 16 * part) = qc[k];
+      *reinterpret_cast<u32x4_t*>(kvt + hh * kQPitch + 16 * part) = qc[k];
     }
   }
   __syncthreads();
   u32x4_t qa[kKb];
 #pragma unroll
-  for (int kb = 0; kb < kKb; ++kb) qa[kb] = *reinterpret_cast<const u32x4_t*>(kvt + j * kKPitch + 16 * (4 * kb + g));
+  for (int kb = 0; kb < kKb; ++kb) qa[kb] = *reinterpret_cast<const u32x4_t*>(kvt + j * kQPitch + 16 * (4 * kb + g));
   __syncthreads(); // the first staging overwrites the tile
 
   float m_run[4], l_run[4];
@@ -310,15 +316,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     //    16ct + 4q .. +3 of token 8g + e (and of 8g + 4 + e for the second).
     {
       const int e = j >> 2, q = j & 3;
-      const uint8_t* vsrc = tile + (8 * g + e) * kKPitch + 2 * (128 * w + 4 * q);
+      const uint8_t* vsrc = tile + (8 * g + e) * kVPitch + 2 * (128 * w + 4 * q);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pt + j * kPPitch + 32 * kb2 + 8 * g);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-          const uint8_t* vp = vsrc + 32 * kb2 * kKPitch + 32 * ct;
+          const uint8_t* vp = vsrc + 32 * kb2 * kVPitch + 32 * ct;
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vp));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vp + 4 * kKPitch));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(vp + 4 * kVPitch));
           const u32x4_t vb = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                               __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   // Normalized rows through LDS (wave w's 16 x 128 block, fp32, row pitch
   // 132), so that the stores are 16 bytes per lane.
   constexpr int kOPitch = 128 + 4;
+  static_assert(4 * 16 * kOPitch * 4 <= kTileBytes, "output staging fits the tile");
   float* ob = reinterpret_cast<float*>(kvt) + w * 16 * kOPitch;
   // This lane's four rows 4g..4g+3: the waves' sums in order, then one
   // reciprocal per row (the outputs take a product; l >= 1, since the row
