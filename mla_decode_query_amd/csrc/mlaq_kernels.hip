@@ -223,14 +223,14 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-// Columns per lane per k row. BF16 weights: 2 (a 4-byte row segment, 32
-// columns and 16 workgroups per head). MXFP8 weights: 4 for M <= 16 (64
-// columns, 8 workgroups per head), 2 for M > 16, where the larger epilogue
-// favours 16 workgroups per head. Chosen by cold-cache timing of the
-// alternatives (2, 4 and 8 columns) in hipGraph loops.
+// Columns per lane per k row: 2 for both weight formats and every M (32
+// columns and 16 workgroups per head; a 4-byte BF16 or 2-byte E4M3 row
+// segment per lane). Chosen by cold-cache timing of 2, 4 and 8 columns in
+// hipGraph loops; for MXFP8 at M <= 16, 4 columns (8 workgroups per head)
+// was ahead once, and is 3-5% behind 2 with the current kernel.
 template <int WF, int MT>
 constexpr int vec_of() {
-  return WF == MLAQ_WEIGHT_BF16 ? 2 : (MT == 1 ? 4 : 2);
+  return 2;
 }
 
 template <int WF, int OF, int MT, int NW>
