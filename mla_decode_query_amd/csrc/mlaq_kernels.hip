@@ -261,9 +261,10 @@ const void* kernel_for(const Variant& v) {
 }
 
 void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
-  int vec = 2;
-  if (v.weight_format == MLAQ_WEIGHT_MXFP8)
-    vec = v.m_tiles == 1 ? vec_of<MLAQ_WEIGHT_MXFP8, 1>() : vec_of<MLAQ_WEIGHT_MXFP8, 2>();
+  // The grid must use the column tile of the very kernel kernel_for() picks.
+  const bool bf = v.weight_format == MLAQ_WEIGHT_BF16, one = v.m_tiles == 1;
+  const int vec = bf ? (one ? vec_of<MLAQ_WEIGHT_BF16, 1>() : vec_of<MLAQ_WEIGHT_BF16, 2>())
+                     : (one ? vec_of<MLAQ_WEIGHT_MXFP8, 1>() : vec_of<MLAQ_WEIGHT_MXFP8, 2>());
   *grid = dim3(unsigned(H * (kLatent / (16 * vec))), 1, 1);
   *block = dim3(unsigned(64 * (v.nope / 32)), 1, 1);
 }
