@@ -256,8 +256,9 @@ typedef struct mlaq_attn_args {
 /* Workspace bytes for a plan (0 when num_splits = 1, or for an invalid plan). */
 size_t mlaq_attn_workspace_size(int M, int H, int num_splits, int partial_dtype);
 /* Split count that fills `device` for M sequences of at most max_seq_len
- * tokens (M * num_splits at most one workgroup per compute unit, ranges of
- * at least 256 tokens, at least 1); written to *num_splits. */
+ * tokens (M * num_splits at most two split workgroups per compute unit,
+ * ranges of at least 256 tokens, at most MLAQ_ATTN_MAX_SPLITS, at least 1);
+ * written to *num_splits. */
 int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits);
 int mlaq_attn_plan_supported(int num_heads, int page_size, int num_splits, int partial_dtype, const char* arch);
 int mlaq_attn_can_implement(int num_heads, int page_size, int num_splits, int partial_dtype, int device);
