@@ -265,6 +265,32 @@ def test_attn_graph_replay_with_mutated_inputs():
         assert_attn_parity(got, lse, oracle_run(cur, S, pd), cur, S, pd, f"replay {seed}")
 
 
+def test_attn_two_streams_at_once():
+    """Two calls in flight together on two streams, each with its own
+    workspace: the library keeps no state between calls, so each result is
+    bit-identical to the same call made alone."""
+    H = 16
+    a_inp = cached_inputs(8910, H, [1500, 300, 64, 9])
+    b_inp = cached_inputs(8911, H, [2000, 7, 640])
+    da, db = Dev(a_inp), Dev(b_inp)
+    alone_a, _ = run_attn(da, a_inp.softmax_scale, 6, BF16P)
+    alone_b, _ = run_attn(db, b_inp.softmax_scale, 3, FP32P)
+    outs, wss = [], []
+    for d, S, pd in ((da, 6, BF16P), (db, 3, FP32P)):
+        outs.append(torch.empty((d.M, H, 512), dtype=torch.bfloat16, device="cuda"))
+        wss.append(torch.empty((mq.mlaq_attn_workspace_size(d.M, H, S, pd),), dtype=torch.uint8, device="cuda"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            mq.mlaq_attn_run(da.q, da.kv, da.bt, da.sl, outs[0], a_inp.softmax_scale, 6, BF16P, wss[0])
+        with torch.cuda.stream(s2):
+            mq.mlaq_attn_run(db.q, db.kv, db.bt, db.sl, outs[1], b_inp.softmax_scale, 3, FP32P, wss[1])
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(outs[0]), alone_a)
+        assert np.array_equal(out_bits(outs[1]), alone_b)
+
+
 def test_attn_can_implement_and_split_heuristic():
     assert mq.mlaq_attn_can_implement(16, 64, 16)
     assert mq.mlaq_attn_can_implement(11, 1, 256, mq.MLAQ_PARTIAL_FP32)
