@@ -72,6 +72,19 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+// Two E4M3 bytes of `word` (bytes 0-1, or 2-3 with hi) times `scale` as a
+// packed bf16 pair (low half = the lower byte), in one gfx950 instruction
+// (v_cvt_scalef32_pk_bf16_fp8). With scale = e8m0_scale(s) this is the exact
+// bf16 of every code's value times 2^(s-127) for s in 3..254 (checked bit for
+// bit against the fp32 conversion and product for all 256 codes and all 256
+// scale bytes); below that the result is a bf16 subnormal, rounded to nearest.
+__device__ __forceinline__ uint32_t e4m3x2_scaled_bf16(uint32_t word, float scale, bool hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(word), scale, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(word), scale, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------------------
 // Loads
 // ---------------------------------------------------------------------------

@@ -33,10 +33,10 @@
 // workgroups copy q_pe into columns 512..575 of the row, storing it before
 // they wait for their weights.
 //
-// MXFP8 weights are decoded in registers: v_cvt_pk_f32_fp8 gives the exact
-// fp32 value of each E4M3 byte, the product with 2^(S-127) is exact, and the
-// top half of that fp32 is its exact bf16. The bf16 MFMA then forms exact
-// products with q_nope, as the pages' exact dequantization requires.
+// MXFP8 weights are decoded in registers: v_cvt_scalef32_pk_bf16_fp8 turns
+// two E4M3 bytes and the 2^(S-127) scale into their exact bf16 values in one
+// instruction. The bf16 MFMA then forms exact products with q_nope, as the
+// pages' exact dequantization requires.
 #include "mlaq.h"
 #include "mlaq_device.h"
 #include "mlaq_internal.h"
@@ -159,25 +159,21 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
             __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
     }
   } else {
-    // Exact decode: fp32(E4M3) * 2^(S-127), whose top 16 bits are its bf16.
-    uint32_t wf[8][VEC];
+    // Exact decode, one scaled conversion per column pair and row: bf16 of
+    // E4M3 * 2^(S-127), laid out as the BF16 path's row dwords.
+    uint32_t wb[8][VEC / 2];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float s = e8m0_scale(sc[r]);
 #pragma unroll
-      for (int e = 0; e < VEC; e += 2) {
-        const int word = int(wr[r][e >> 2]);
-        const f32x2_t v = ((e >> 1) & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
-                                         : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        wf[r][e] = __float_as_uint(v[0] * s);
-        wf[r][e + 1] = __float_as_uint(v[1] * s);
-      }
+      for (int e = 0; e < VEC; e += 2) wb[r][e >> 1] = e4m3x2_scaled_bf16(wr[r][e >> 2], s, (e >> 1) & 1);
     }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
       u32x4_t b;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wf[2 * p + 1][i], wf[2 * p][i], 0x07060302u);
+      for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wb[2 * p + 1][i >> 1], wb[2 * p][i >> 1], sel);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

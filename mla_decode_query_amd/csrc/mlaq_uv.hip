@@ -25,8 +25,9 @@
 // once.
 //
 // MXFP8: a lane loads 8 E4M3 bytes and the one E8M0 byte of their 32-group;
-// v_cvt_pk_f32_fp8 times 2^(S-127) is exact and its top half is the exact
-// bf16, so the MFMA forms exact products as the oracle's dequantization does.
+// v_cvt_scalef32_pk_bf16_fp8 gives the exact bf16 of each byte times
+// 2^(S-127), so the MFMA forms exact products as the oracle's dequantization
+// does.
 #include "mlaq.h"
 #include "mlaq_device.h"
 #include "mlaq_internal.h"
@@ -96,16 +97,12 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   for (int kb = 0; kb < 4; ++kb) {
     u32x4_t b = wb[kb];
     if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
-      // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16 pairs.
+      // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16
+      // pairs, one scaled conversion each.
       const float s = e8m0_scale(sc[kb]);
       u32x4_t d;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int word = int(b[p >> 1]);
-        const f32x2_t f = (p & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
-                                  : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        d[p] = __builtin_amdgcn_perm(__float_as_uint(f[1] * s), __float_as_uint(f[0] * s), 0x07060302u);
-      }
+      for (int p = 0; p < 4; ++p) d[p] = e4m3x2_scaled_bf16(b[p >> 1], s, p & 1);
       b = d;
     }
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[kb]),
