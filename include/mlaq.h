@@ -44,7 +44,7 @@ extern "C" {
 
 /* Output element types. */
 #define MLAQ_OUT_BF16 0 /* bf16 [M,H,576] */
-#define MLAQ_OUT_E4M3 1 /* OCP E4M3FN [M,H,576], scaled by 1/q_scale, saturating at +-448 */
+#define MLAQ_OUT_E4M3 1 /* OCP E4M3FN [M,H,576]: value / q_scale, saturating at +-448 */
 
 /* Status codes. */
 #define MLAQ_OK 0
@@ -110,7 +110,11 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
  *   w_scales E8M0 bytes [H,128,16]: byte [h,k,j] scales columns 32j..32j+31
  *            of row k; required for MXFP8, must be NULL for BF16 weights
  *   q_scale  device fp32[1], 4-byte aligned; required for E4M3 output, must be
- *            NULL for BF16 output (the BF16 output takes no scale)
+ *            NULL for BF16 output (the BF16 output takes no scale). Every
+ *            value is accepted: x / q_scale is the IEEE fp32 quotient (so 0,
+ *            inf and NaN scales act as IEEE division says), then rounded to
+ *            nearest-even E4M3, finite or infinite results past 448 giving
+ *            +-448 and NaN giving 0x7F / 0xFF
  *   out      bf16 or E4M3 [M,H,576], contiguous, 16-byte aligned, must not
  *            overlap any input
  *   M        tokens, 0..32 (M = 0 is a no-op that returns MLAQ_OK)
@@ -262,7 +266,8 @@ size_t mlaq_attn_workspace_size(int M, int H, int num_splits, int partial_dtype)
 int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits);
 int mlaq_attn_plan_supported(int num_heads, int page_size, int num_splits, int partial_dtype, const char* arch);
 int mlaq_attn_can_implement(int num_heads, int page_size, int num_splits, int partial_dtype, int device);
-/* Loads both kernels of a partial dtype (and the one-split kernel). */
+/* Loads the split kernel of a partial dtype, every merge kernel shape it may
+ * pair with, and the one-split kernel. */
 int mlaq_attn_prewarm(int partial_dtype, int device);
 int mlaq_attn_run(const mlaq_attn_args* args, void* stream);
 

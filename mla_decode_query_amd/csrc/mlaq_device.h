@@ -54,8 +54,10 @@ __device__ __forceinline__ uint32_t e4m3x4_satfinite(float v0, float v1, float v
 // is within one ulp of y / b, the residual y - q0 * b is exact in one FMA,
 // and one FMA correction then gives RN(y / b) (Markstein's correction step).
 // Checked against IEEE division for every finite bf16 y and 40,000 divisors
-// with 2^-64 <= |b| < 2^65. For |y| < 2^-100 the residual can underflow; such
-// quotients are far below the smallest E4M3 step, and q0 carries their sign.
+// with 2^-64 <= |b| < 2^65. Valid while rb is a normal number; for
+// |y| < 2^-100 the residual can underflow, and q0 (which carries the sign)
+// is returned. Callers that encode the quotient to E4M3 use it only for
+// divisors accepted by div_rn_covers.
 __device__ __forceinline__ float div_rn(float y, float b, float rb) {
   const float q0 = y * rb;
   const float rho = __builtin_fmaf(-q0, b, y);
@@ -64,6 +66,16 @@ __device__ __forceinline__ float div_rn(float y, float b, float rb) {
   // zero y (which also keeps the sign of a zero quotient).
   const bool plain = !(__builtin_fabsf(y) >= 0x1p-100f) || !(__builtin_fabsf(q0) <= 0x1.fffffep127f);
   return plain ? q0 : q1;
+}
+
+// Divisors for which div_rn followed by the E4M3 encoder gives the code of
+// the IEEE quotient for every y: 1/b is then a normal fp32, and a quotient of
+// |y| < 2^-100 stays at most 2^-10, which encodes to a signed zero whether or
+// not its last bit is right. Others (0, subnormal or huge b, inf, NaN) take
+// the IEEE division.
+__device__ __forceinline__ bool div_rn_covers(float b) {
+  const float ab = __builtin_fabsf(b);
+  return ab >= 0x1p-90f && ab <= 0x1p126f;
 }
 
 // E8M0 scale byte -> 2^(s-127) as fp32 (0xff -> NaN).

@@ -46,6 +46,11 @@ namespace {
 
 using namespace dev;
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // ---------------------------------------------------------------------------
 // The fused kernel
 // ---------------------------------------------------------------------------
@@ -121,101 +126,121 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     qs = *a.q_scale;
     rqs = 1.0f / qs;
   }
-  if (has_pe) {
-    const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
-    if constexpr (OF == MLAQ_OUT_BF16) {
-      *at_byte<u32x4_t>(a.out, 2 * o) = pe_v;
-    } else {
-      float x[8];
+  // Everything from here on, in two copies: x / q_scale by the one-FMA
+  // correction (the scales where it is exact), or by IEEE division (0, inf,
+  // NaN, subnormal or huge scales). The choice is uniform over the launch, so
+  // the usual copy runs as straight-line code.
+  auto tail = [&](auto ieee_div) __attribute__((always_inline)) {
+    auto quot = [&](float (&x)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        x[c] = div_rn(__uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16), qs, rqs);
-      u32x2_t v;
-      v[0] = e4m3x4_satfinite(x[0], x[1], x[2], x[3]);
-      v[1] = e4m3x4_satfinite(x[4], x[5], x[6], x[7]);
-      *at_byte<u32x2_t>(a.out, o) = v;
+      for (int c = 0; c < 4; ++c) x[c] = decltype(ieee_div)::value ? x[c] / qs : div_rn(x[c], qs, rqs);
+    };
+    if (has_pe) {
+      const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
+      if constexpr (OF == MLAQ_OUT_BF16) {
+        *at_byte<u32x4_t>(a.out, 2 * o) = pe_v;
+      } else {
+        float x[2][4];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          x[c >> 2][c & 3] = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
+        quot(x[0]);
+        quot(x[1]);
+        u32x2_t v;
+        v[0] = e4m3x4_satfinite(x[0][0], x[0][1], x[0][2], x[0][3]);
+        v[1] = e4m3x4_satfinite(x[1][0], x[1][1], x[1][2], x[1][3]);
+        *at_byte<u32x2_t>(a.out, o) = v;
+      }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
+    __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
 
-  // 5. Contraction over this wave's 32 k rows.
-  f32x4_t acc[MT][VEC];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if constexpr (WF == MLAQ_WEIGHT_BF16) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      u32x4_t b;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        b[p] = __builtin_amdgcn_perm(wr[2 * p + 1][i >> 1], wr[2 * p][i >> 1], sel);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
-    }
-  } else {
-    // Exact decode, one scaled conversion per column pair and row: bf16 of
-    // E4M3 * 2^(S-127), laid out as the BF16 path's row dwords.
-    uint32_t wb[8][VEC / 2];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float s = e8m0_scale(sc[r]);
-#pragma unroll
-      for (int e = 0; e < VEC; e += 2) wb[r][e >> 1] = e4m3x2_scaled_bf16(wr[r][e >> 2], s, (e >> 1) & 1);
-    }
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      u32x4_t b;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wb[2 * p + 1][i >> 1], wb[2 * p][i >> 1], sel);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
-    }
-  }
-
-  // 5b. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
-  //    columns VEC*j + i.
-  {
-    float* pw = part + wave * MROWS * LDW;
+    // 5. Contraction over this wave's 32 k rows.
+    f32x4_t acc[MT][VEC];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float* dst = pw + (16 * t + 4 * g + r) * LDW + VEC * j;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) dst[i] = acc[t][i][r];
-      }
-  }
-  __syncthreads();
+      for (int i = 0; i < VEC; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // 6. Epilogue: sum the k slices in a fixed order, round, convert and
-  //    store; each thread finishes 4 consecutive columns of one token.
-  constexpr int GPR = WCOLS / 4;
-  for (int x = tid; x < M * GPR; x += THREADS) {
-    const int m = x / GPR, cg = x - m * GPR;
-    const int off = m * LDW + 4 * cg;
-    f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
+    if constexpr (WF == MLAQ_WEIGHT_BF16) {
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
-    const uint32_t o = __umul24(m, a.out_sm) + __umul24(h, a.out_sh) + c0 + 4 * cg;
-    const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
-    const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
-    if constexpr (OF == MLAQ_OUT_BF16) {
-      *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{b01, b23};
+      for (int i = 0; i < VEC; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t b;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          b[p] = __builtin_amdgcn_perm(wr[2 * p + 1][i >> 1], wr[2 * p][i >> 1], sel);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
+      }
     } else {
-      const float y0 = __uint_as_float(b01 << 16), y1 = __uint_as_float(b01 & 0xffff0000u);
-      const float y2 = __uint_as_float(b23 << 16), y3 = __uint_as_float(b23 & 0xffff0000u);
-      *at_byte<uint32_t>(a.out, o) =
-          e4m3x4_satfinite(div_rn(y0, qs, rqs), div_rn(y1, qs, rqs), div_rn(y2, qs, rqs), div_rn(y3, qs, rqs));
+      // Exact decode, one scaled conversion per column pair and row: bf16 of
+      // E4M3 * 2^(S-127), laid out as the BF16 path's row dwords.
+      uint32_t wb[8][VEC / 2];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float s = e8m0_scale(sc[r]);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) wb[r][e >> 1] = e4m3x2_scaled_bf16(wr[r][e >> 2], s, (e >> 1) & 1);
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t b;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wb[2 * p + 1][i >> 1], wb[2 * p][i >> 1], sel);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
+      }
     }
+
+    // 5b. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
+    //    columns VEC*j + i.
+    {
+      float* pw = part + wave * MROWS * LDW;
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* dst = pw + (16 * t + 4 * g + r) * LDW + VEC * j;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) dst[i] = acc[t][i][r];
+        }
+    }
+    __syncthreads();
+
+    // 6. Epilogue: sum the k slices in a fixed order, round, convert and
+    //    store; each thread finishes 4 consecutive columns of one token.
+    constexpr int GPR = WCOLS / 4;
+    for (int x = tid; x < M * GPR; x += THREADS) {
+      const int m = x / GPR, cg = x - m * GPR;
+      const int off = m * LDW + 4 * cg;
+      f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
+      const uint32_t o = __umul24(m, a.out_sm) + __umul24(h, a.out_sh) + c0 + 4 * cg;
+      const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
+      const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
+      if constexpr (OF == MLAQ_OUT_BF16) {
+        *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{b01, b23};
+      } else {
+        float y[4] = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u), __uint_as_float(b23 << 16),
+                      __uint_as_float(b23 & 0xffff0000u)};
+        quot(y);
+        *at_byte<uint32_t>(a.out, o) = e4m3x4_satfinite(y[0], y[1], y[2], y[3]);
+      }
+    }
+  };
+  if constexpr (OF == MLAQ_OUT_E4M3) {
+    if (__builtin_expect(div_rn_covers(qs), 1))
+      tail(Flag<false>{});
+    else
+      tail(Flag<true>{});
+  } else {
+    tail(Flag<false>{});
   }
 }
 
