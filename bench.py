@@ -11,15 +11,17 @@ the 64 fused calls captured as one hipGraph. Six copies of the 64 weight sets
 not from the 256 MB Infinity Cache. It runs every step of the path: dispatch,
 weight streaming, q_nope staging, MXFP8 decode, contraction, rounding, the
 E4M3 epilogue, the q_pe append and the step composition. Per-layer seeds are
-100 * 1004 + layer (see workloads.make_inputs for the recipe).
+100 * 1004 + layer (see workloads.make_inputs for the recipe). The step's
+calls pass MLAQ_CACHE_STREAM (weights read once per step, cold); the same
+step with the default hint is timed and reported beside it.
 
 Printed JSON line (stdout, one line):
   value       algorithmic HBM bytes of the step / step time, in GB/s
   ms_per_step hipEvent time per replayed step
-  roofline    the dominant kernel (BF16-weight layer, M=32, E4M3 out): its
-              algorithmic bytes per launch / its average launch duration,
-              timed live with hipEvents over back-to-back cold launches,
-              against the 8 TB/s HBM peak
+  roofline    the dominant kernel (BF16-weight layer, M=32, E4M3 out,
+              streaming hint): its algorithmic bytes per launch / its average
+              launch duration, timed live with hipEvents over back-to-back
+              cold launches, against the 8 TB/s HBM peak
   per_call    warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
               MXFP8 weights (BF16 output), with the staged torch baseline
   pages_shape the pages' own workload (K=192, H=8, M=1, BF16, 78 layers,
@@ -122,12 +124,17 @@ class Layer:
         return dev_u8(torch, self.w_host), dev_u8(torch, self.s_host)
 
 
-def step_graph(torch, mq, layers, wcopy, stream):
+def step_graph(torch, mq, layers, wcopy, stream, cache_hint=None, only_wf=None):
+    """One hipGraph of the step's layers (or of those with weight format
+    only_wf) over one weight copy. A decode step reads each layer's weights
+    once, cold, so the default is the streaming cache hint."""
+    hint = mq.MLAQ_CACHE_STREAM if cache_hint is None else cache_hint
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
             for L, (w, s) in zip(layers, wcopy):
-                mq.mlaq_run(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3)
+                if only_wf is None or L.wf == only_wf:
+                    mq.mlaq_run_ex(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3, cache_hint=hint)
     return g
 
 
@@ -177,25 +184,28 @@ def decode_step_leg(torch, mq, wl, args):
     ms = time_graphs(torch, graphs, args.steps, args.warmup)
     step_bytes = sum(L.bytes for L in layers)
     log(f"[bench] fused step: {ms * 1e3:.2f} us/step, {ms * 1e3 / LAYERS:.3f} us/layer, "
-        f"{step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+        f"{step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s (streaming cache hint)")
+    # The same step with the default cache hint (ordinary loads and stores).
+    dflt = [step_graph(torch, mq, layers, copies[c], stream, mq.MLAQ_CACHE_DEFAULT) for c in range(COPIES)]
+    torch.cuda.synchronize()
+    ms_default = time_graphs(torch, dflt, args.steps, args.warmup)
+    log(f"[bench] fused step, default cache hint: {ms_default * 1e3:.2f} us/step")
+    del dflt
 
     # Dominant kernel alone: the 32 BF16-weight layers back to back (cold).
-    dom_graphs = []
-    for c in range(COPIES):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
-                for L, (w, s) in zip(layers, copies[c]):
-                    if L.wf == mq.MLAQ_WEIGHT_BF16:
-                        mq.mlaq_run(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3)
-        dom_graphs.append(g)
-    torch.cuda.synchronize()
     n_bf = sum(1 for L in layers if L.wf == mq.MLAQ_WEIGHT_BF16)
-    dom_ms = time_graphs(torch, dom_graphs, args.steps, args.warmup, per_step_units=n_bf)
     dom_bytes = wl.algorithmic_bytes(M_STEP, H, mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_E4M3)
+    dom = {}
+    for hint in (mq.MLAQ_CACHE_DEFAULT, mq.MLAQ_CACHE_STREAM):
+        dom_graphs = [step_graph(torch, mq, layers, copies[c], stream, hint, mq.MLAQ_WEIGHT_BF16)
+                      for c in range(COPIES)]
+        torch.cuda.synchronize()
+        dom[hint] = time_graphs(torch, dom_graphs, args.steps, args.warmup, per_step_units=n_bf)
+        del dom_graphs
+    dom_ms = dom[mq.MLAQ_CACHE_STREAM]
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
-    log(f"[bench] dominant kernel (bf16 W, M=32, E4M3): {dom_ms * 1e3:.3f} us/launch, {dom_gbs:.1f} GB/s")
-    del dom_graphs
+    log(f"[bench] dominant kernel (bf16 W, M=32, E4M3): {dom_ms * 1e3:.3f} us/launch, {dom_gbs:.1f} GB/s "
+        f"(streaming hint; default hint {dom[mq.MLAQ_CACHE_DEFAULT] * 1e3:.3f} us)")
 
     # Staged path of the same step: bmm + copy + copy + E4M3 quantization.
     staged_graphs = []
@@ -220,7 +230,8 @@ def decode_step_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     floors = floors_leg(torch, mq, layers, copies, stream, args)
     return {
-        "layers": layers, "ms": ms, "step_bytes": step_bytes, "dom_ms": dom_ms, "dom_bytes": dom_bytes,
+        "layers": layers, "ms": ms, "ms_default_hint": ms_default, "step_bytes": step_bytes, "dom_ms": dom_ms,
+        "dom_ms_default_hint": dom[mq.MLAQ_CACHE_DEFAULT], "dom_bytes": dom_bytes,
         "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes, "floors": floors,
     }
 
@@ -337,7 +348,7 @@ def pages_shape_leg(torch, mq, wl, args):
             with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
                 for d, w in zip(lay, wc[c]):
                     mq.mlaq_run_ex(d["q_hm"].transpose(0, 1), d["pe"], w, None, None, d["out"],
-                                   mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+                                   mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16, cache_hint=mq.MLAQ_CACHE_STREAM)
         return g
 
     def staged_graph(c):
@@ -726,10 +737,13 @@ def main():
                    "heads": H, "tokens": M_STEP, "layers": LAYERS, "nope": 128, "latent": 512, "rope": 64,
                    "bytes_per_step": step["step_bytes"]},
         "us_per_layer": round(ms * 1e3 / LAYERS, 4),
+        "cache_hint": "stream (weights read once per step); default-hint step "
+                      f"{step['ms_default_hint'] * 1e3:.2f} us",
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles>",
-                     "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"]},
+                     "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles, streaming hint>",
+                     "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"],
+                     "us_per_launch_default_hint": round(step["dom_ms_default_hint"] * 1e3, 4)},
         "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3)},
         "floors": step["floors"],
         "per_call": per_call,

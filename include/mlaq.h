@@ -46,6 +46,10 @@ extern "C" {
 #define MLAQ_OUT_BF16 0 /* bf16 [M,H,576] */
 #define MLAQ_OUT_E4M3 1 /* OCP E4M3FN [M,H,576]: value / q_scale, saturating at +-448 */
 
+/* Cache hints of mlaq_run_ex (timing only; results are identical). */
+#define MLAQ_CACHE_DEFAULT 0 /* weights may stay cached between calls */
+#define MLAQ_CACHE_STREAM 1  /* weights read once per step, cold in HBM */
+
 /* Status codes. */
 #define MLAQ_OK 0
 #define MLAQ_ERR_UNSUPPORTED 1 /* plan outside the fused path: keep the staged path */
@@ -84,7 +88,8 @@ int mlaq_can_implement(int num_heads, int max_m, int nope_dim, int latent_dim, i
 
 /*
  * mlaq_prewarm -- load the kernels that serve the given token counts
- * (`m_regimes[0..n_regimes)`, each in 1..32, for both nope widths) for H
+ * (`m_regimes[0..n_regimes)`, each in 1..32, for both nope widths and both
+ * cache hints) for H
  * heads on `device`, and
  * cache the device's architecture, so later mlaq_run calls do no first-use
  * work and can be captured into a hipGraph. Deduplicates regimes that share a
@@ -151,6 +156,20 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
  * times its extent); the output's address span disjoint from every input's.
  * nope_dim must be 128 or 192 (else MLAQ_ERR_UNSUPPORTED). Everything else is
  * as for mlaq_run.
+ *
+ * cache_hint tells the kernel how the weight slab will be used next; it
+ * changes timing only, never a result bit (else MLAQ_ERR_INVALID_ARG):
+ *   MLAQ_CACHE_DEFAULT (0, what mlaq_run uses): ordinary loads and stores, so
+ *       a weight set that fits in the caches stays there across calls (the
+ *       same layer called back to back);
+ *   MLAQ_CACHE_STREAM (1): the weights are read once per decode step and are
+ *       cold in HBM when the call starts (a model's layers in turn, as in
+ *       serving). BF16 weight rows are then loaded, and the output stored,
+ *       with the nontemporal hint, which shortens a cold call and lengthens a
+ *       warm one. MXFP8 weights ignore the hint: their 32-byte row segments
+ *       share each 128-byte line among four workgroups, and the hint made
+ *       those calls slower.
+ * A zero-initialised struct gets MLAQ_CACHE_DEFAULT.
  */
 typedef struct mlaq_run_args {
   const void* q_nope;
@@ -163,6 +182,7 @@ typedef struct mlaq_run_args {
   void* out;
   int64_t out_stride_m, out_stride_h;
   int M, H, nope_dim, weight_format, out_dtype;
+  int cache_hint; /* MLAQ_CACHE_*; occupies what was tail padding, so the size is unchanged */
 } mlaq_run_args;
 
 int mlaq_run_ex(const mlaq_run_args* args, void* stream);

@@ -39,6 +39,7 @@ LIB_PATH = _PKG / "libmlaq.so"
 
 MLAQ_WEIGHT_BF16, MLAQ_WEIGHT_MXFP8 = 0, 1
 MLAQ_OUT_BF16, MLAQ_OUT_E4M3 = 0, 1
+MLAQ_CACHE_DEFAULT, MLAQ_CACHE_STREAM = 0, 1
 MLAQ_OK, MLAQ_ERR_UNSUPPORTED, MLAQ_ERR_INVALID_ARG, MLAQ_ERR_DEVICE = 0, 1, 2, 3
 NOPE_DIM, LATENT_DIM, ROPE_DIM, MAX_M = 128, 512, 64, 32
 NOPE_DIM_GLM = 192
@@ -62,7 +63,7 @@ class RunArgs(ctypes.Structure):
                 ("w", ctypes.c_void_p), ("w_scales", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("out_stride_m", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
                 ("M", ctypes.c_int), ("H", ctypes.c_int), ("nope_dim", ctypes.c_int),
-                ("weight_format", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+                ("weight_format", ctypes.c_int), ("out_dtype", ctypes.c_int), ("cache_hint", ctypes.c_int)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -236,11 +237,13 @@ def _expect_view(t, name, dtype, shape, device):
 
 def mlaq_run_ex(q_nope: torch.Tensor, q_pe: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None,
                 q_scale: torch.Tensor | None, out: torch.Tensor, weight_format: int, out_dtype: int,
-                stream: torch.cuda.Stream | None = None) -> None:
+                stream: torch.cuda.Stream | None = None, cache_hint: int = MLAQ_CACHE_DEFAULT) -> None:
     """Like ``mlaq_run`` but ``q_nope`` ([M,H,K], K = 128 or 192), ``q_pe`` and
     ``out`` may be strided views (e.g. ``q.transpose(0, 1)`` of a head-major
     [H,M,K] tensor, or ``ws[..., :576]`` of a wider workspace). Weights stay
-    contiguous [H,K,512] (and [H,K,16] scales)."""
+    contiguous [H,K,512] (and [H,K,16] scales). ``cache_hint``:
+    ``MLAQ_CACHE_STREAM`` when the weights are read once per decode step (cold
+    in HBM), ``MLAQ_CACHE_DEFAULT`` otherwise; results are identical."""
     if q_nope.dim() != 3:
         raise ValueError("q_nope must be [M,H,K]")
     M, H, K = (int(x) for x in q_nope.shape)
@@ -262,7 +265,7 @@ def mlaq_run_ex(q_nope: torch.Tensor, q_pe: torch.Tensor, w: torch.Tensor, w_sca
     args = RunArgs(q_nope.data_ptr(), q_sm, q_sh, q_pe.data_ptr(), pe_sm, pe_sh, w.data_ptr(),
                    None if w_scales is None else w_scales.data_ptr(),
                    None if q_scale is None else q_scale.data_ptr(), out.data_ptr(), o_sm, o_sh,
-                   M, H, K, weight_format, out_dtype)
+                   M, H, K, weight_format, out_dtype, cache_hint)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     _check(library().mlaq_run_ex(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
 

@@ -180,11 +180,13 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != device) e = hipSetDevice(device);
-    for (int K : {mlaq::kNope, mlaq::kNopeGlm}) {
-      hipFuncAttributes attr;
-      if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, mlaq::kernel_for(mlaq::variant_for(weight_format, out_dtype, m_regimes[i], K)));
-    }
+    for (int K : {mlaq::kNope, mlaq::kNopeGlm})
+      for (int hint : {MLAQ_CACHE_DEFAULT, MLAQ_CACHE_STREAM}) {
+        hipFuncAttributes attr;
+        if (e == hipSuccess)
+          e = hipFuncGetAttributes(&attr,
+                                   mlaq::kernel_for(mlaq::variant_for(weight_format, out_dtype, m_regimes[i], K, hint)));
+      }
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
   }
@@ -198,6 +200,8 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   const int M = a.M, H = a.H, K = a.nope_dim;
   if (!known_weight_format(a.weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", a.weight_format);
   if (!known_out_dtype(a.out_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown out_dtype %d", a.out_dtype);
+  if (a.cache_hint != MLAQ_CACHE_DEFAULT && a.cache_hint != MLAQ_CACHE_STREAM)
+    return fail(MLAQ_ERR_INVALID_ARG, "unknown cache_hint %d", a.cache_hint);
   if (!supported_heads(H)) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d not in {8, 11, 16}", H);
   if (M < 0 || M > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "M=%d outside 0..32", M);
   if (K != MLAQ_NOPE_DIM && K != MLAQ_NOPE_DIM_GLM) return fail(MLAQ_ERR_UNSUPPORTED, "nope_dim=%d not 128 or 192", K);
@@ -240,7 +244,7 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   st = plan_for(H, M, K, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, a.weight_format, a.out_dtype, arch);
   if (st != MLAQ_OK) return st;
 
-  const mlaq::Variant v = mlaq::variant_for(a.weight_format, a.out_dtype, M, K);
+  const mlaq::Variant v = mlaq::variant_for(a.weight_format, a.out_dtype, M, K, a.cache_hint);
   const void* fn = mlaq::kernel_for(v);
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
@@ -275,6 +279,7 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
   a.nope_dim = mlaq::kNope;
   a.weight_format = weight_format;
   a.out_dtype = out_dtype;
+  a.cache_hint = MLAQ_CACHE_DEFAULT;
   return mlaq_run_ex(&a, stream);
 }
 

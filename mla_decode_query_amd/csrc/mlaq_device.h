@@ -102,12 +102,17 @@ __device__ __forceinline__ uint32_t e4m3x2_scaled_bf16(uint32_t word, float scal
 // ---------------------------------------------------------------------------
 
 // One lane's segment of one k row: RB bytes (2, 4, 8 or 16) into dwords.
-template <int RB>
+// NT marks a 4-byte load nontemporal (streamed data, read once).
+template <int RB, bool NT = false>
 __device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[(RB + 3) / 4]) {
+  static_assert(!NT || RB == 4, "nontemporal row loads are 4 bytes wide");
   if constexpr (RB == 2) {
     d[0] = *reinterpret_cast<const uint16_t*>(p);
   } else if constexpr (RB == 4) {
-    d[0] = *reinterpret_cast<const uint32_t*>(p);
+    if constexpr (NT)
+      d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    else
+      d[0] = *reinterpret_cast<const uint32_t*>(p);
   } else if constexpr (RB == 8) {
     const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
     d[0] = v[0];

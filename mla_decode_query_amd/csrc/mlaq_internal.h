@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mlaq.h"
+
 namespace mlaq {
 
 constexpr int kNope = 128;   // K of the contiguous entry point (mlaq_run)
@@ -38,10 +40,13 @@ struct Variant {
   int out_dtype;     // MLAQ_OUT_*
   int m_tiles;       // 16-token tiles: 1 (M <= 16) or 2 (M <= 32)
   int nope;          // K: 128 or 192
+  bool stream;       // nontemporal weight loads and output stores (BF16 weights only)
 };
 
-inline Variant variant_for(int weight_format, int out_dtype, int M, int nope) {
-  return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2, nope};
+// MLAQ_CACHE_STREAM selects the nontemporal kernels for BF16 weights; MXFP8
+// weights always use the ordinary ones (the hint measured slower there).
+inline Variant variant_for(int weight_format, int out_dtype, int M, int nope, int cache_hint = MLAQ_CACHE_DEFAULT) {
+  return Variant{weight_format, out_dtype, M <= 16 ? 1 : 2, nope, cache_hint == MLAQ_CACHE_STREAM && weight_format == MLAQ_WEIGHT_BF16};
 }
 
 // V up-projection arguments (all contiguous).

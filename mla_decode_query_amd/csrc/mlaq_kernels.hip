@@ -33,6 +33,15 @@
 // workgroups copy q_pe into columns 512..575 of the row, storing it before
 // they wait for their weights.
 //
+// Cache policy. A decode step reads each layer's weights once, cold in HBM;
+// the MLAQ_CACHE_STREAM kernels (template flag NT, BF16 weights only) load
+// the weight rows and store the output with the nontemporal hint, which
+// shortened the cold BF16-weight launch by 8-10% in same-box A/B runs
+// (identical output bits) and lengthened back-to-back calls on one cached
+// weight set by 5-14%, hence a caller's hint rather than the only form.
+// MXFP8 rows are 32-byte segments whose 128-byte lines four workgroups share;
+// there every nontemporal form was slower, so those kernels have no NT form.
+//
 // MXFP8 weights are decoded in registers: v_cvt_scalef32_pk_bf16_fp8 turns
 // two E4M3 bytes and the 2^(S-127) scale into their exact bf16 values in one
 // instruction. The bf16 MFMA then forms exact products with q_nope, as the
@@ -46,6 +55,15 @@ namespace {
 
 using namespace dev;
 
+// An output store, nontemporal in the NT kernels.
+template <bool NT, typename T>
+__device__ __forceinline__ void store_out(T* p, T v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 template <bool B>
 struct Flag {
   static constexpr bool value = B;
@@ -55,7 +73,7 @@ struct Flag {
 // The fused kernel
 // ---------------------------------------------------------------------------
 
-template <int WF, int OF, int MT, int VEC, int NW>
+template <int WF, int OF, int MT, int VEC, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   constexpr int K = 32 * NW;                            // reduction width
   constexpr int THREADS = 64 * NW;
@@ -68,6 +86,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
   static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
   static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 2 == 0, "E4M3 columns are decoded in pairs");
+  static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 weight rows are streamed nontemporally");
   __shared__ __attribute__((aligned(16))) float part[NW * MROWS * LDW];
 
   const int tid = threadIdx.x;
@@ -98,7 +117,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     __builtin_assume(off < (1u << 22));
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      load_row<RB>(static_cast<const uint8_t*>(a.w) + (off + uint32_t(r) * kLatent * ESZ), wr[r]);
+      load_row<RB, NT>(static_cast<const uint8_t*>(a.w) + (off + uint32_t(r) * kLatent * ESZ), wr[r]);
   }
   uint32_t sc[8];
   if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
@@ -138,7 +157,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     if (has_pe) {
       const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
       if constexpr (OF == MLAQ_OUT_BF16) {
-        *at_byte<u32x4_t>(a.out, 2 * o) = pe_v;
+        store_out<NT>(at_byte<u32x4_t>(a.out, 2 * o), pe_v);
       } else {
         float x[2][4];
 #pragma unroll
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
         u32x2_t v;
         v[0] = e4m3x4_satfinite(x[0][0], x[0][1], x[0][2], x[0][3]);
         v[1] = e4m3x4_satfinite(x[1][0], x[1][1], x[1][2], x[1][3]);
-        *at_byte<u32x2_t>(a.out, o) = v;
+        store_out<NT>(at_byte<u32x2_t>(a.out, o), v);
       }
     }
     __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
@@ -225,12 +244,12 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
       const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
       const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
       if constexpr (OF == MLAQ_OUT_BF16) {
-        *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{b01, b23};
+        store_out<NT>(at_byte<u32x2_t>(a.out, 2 * o), u32x2_t{b01, b23});
       } else {
         float y[4] = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u), __uint_as_float(b23 << 16),
                       __uint_as_float(b23 & 0xffff0000u)};
         quot(y);
-        *at_byte<uint32_t>(a.out, o) = e4m3x4_satfinite(y[0], y[1], y[2], y[3]);
+        store_out<NT>(at_byte<uint32_t>(a.out, o), e4m3x4_satfinite(y[0], y[1], y[2], y[3]));
       }
     }
   };
@@ -254,17 +273,21 @@ constexpr int vec_of() {
   return 2;
 }
 
-template <int WF, int OF, int MT, int NW>
+template <int WF, int OF, int MT, int NW, bool NT = false>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>(), NW>);
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>(), NW, NT>);
 }
 
 } // namespace
 
 const void* kernel_for(const Variant& v) {
-#define MLAQ_CASE(WF, OF, MT, K)                                                            \
-  if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT && v.nope == K) \
-    return kernel_ptr<WF, OF, MT, K / 32>();
+#define MLAQ_CASE(WF, OF, MT, K)                                                                 \
+  if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT && v.nope == K) {      \
+    if constexpr (WF == MLAQ_WEIGHT_BF16)                                                  \
+      return v.stream ? kernel_ptr<WF, OF, MT, K / 32, true>() : kernel_ptr<WF, OF, MT, K / 32>(); \
+    else                                                                                   \
+      return v.stream ? nullptr : kernel_ptr<WF, OF, MT, K / 32>();                        \
+  }
 #define MLAQ_CASES(K)                                \
   MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1, K)  \
   MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 2, K)  \

@@ -152,7 +152,7 @@ int main(void) {
   printf("%zu", sizeof(mlaq_run_args));
 #define F(x) printf(" %zu", offsetof(mlaq_run_args, x));
   F(q_nope) F(q_stride_m) F(q_stride_h) F(q_pe) F(pe_stride_m) F(pe_stride_h) F(w) F(w_scales) F(q_scale)
-  F(out) F(out_stride_m) F(out_stride_h) F(M) F(H) F(nope_dim) F(weight_format) F(out_dtype)
+  F(out) F(out_stride_m) F(out_stride_h) F(M) F(H) F(nope_dim) F(weight_format) F(out_dtype) F(cache_hint)
   printf("\n");
   return 0;
 }
@@ -198,10 +198,22 @@ def run_ex(lib, **kw):
     (dict(out_dtype=1), INV, "needs q_scale"),
     (dict(H=12), UNS, "H=12"),
     (dict(M=40), UNS, "M=40"),
+    (dict(cache_hint=2), INV, "cache_hint 2"),
+    (dict(cache_hint=-1), INV, "cache_hint -1"),
 ])
 def test_run_ex_rejects_before_any_device_call(lib, kw, status, msg):
     assert run_ex(lib, **kw) == status
     assert msg in mq.mlaq_last_error()
+
+
+def test_run_args_cache_hint_fills_tail_padding():
+    """cache_hint sits in what was the struct's tail padding: the size is that
+    of the fields before it rounded to 8 bytes, and a zero-initialised struct
+    carries MLAQ_CACHE_DEFAULT."""
+    assert ctypes.sizeof(mq.RunArgs) == 8 * 12 + 4 * 6
+    assert mq.RunArgs.cache_hint.offset == 8 * 12 + 4 * 5
+    assert mq.RunArgs().cache_hint == mq.MLAQ_CACHE_DEFAULT == 0
+    assert mq.MLAQ_CACHE_STREAM == 1
 
 
 def test_run_ex_null_args_and_empty_batch(lib):

@@ -185,3 +185,76 @@ def test_k192_graph_replay_with_strided_views():
         mq.mlaq_run_ex(q_hm.transpose(0, 1), pe, w, None, None, ws2[:, :, :mq.ROW], wf, BF16)
         torch.cuda.synchronize()
         assert torch.equal(ws2, ws)
+
+
+@pytest.mark.parametrize("K", [128, 192])
+@pytest.mark.parametrize("od", [BF16, E4M3])
+@pytest.mark.parametrize("wf", [WEIGHT_BF16, WEIGHT_MXFP8])
+def test_stream_cache_hint(wf, od, K):
+    """MLAQ_CACHE_STREAM (nontemporal weight loads and output stores for BF16
+    weights; the ordinary kernels for MXFP8) changes timing only: every head
+    count and both token tiles give the oracle's parity and the bits of the
+    default hint, into a pitched output whose padding stays untouched."""
+    qs_val = 0.03
+    for H in (8, 11, 16):
+        for M in (1, 9, 17, 32):
+            inp = inputs(SEED["c2"] + 7, H, wf, K).take(M)
+            w, s = weights(inp)
+            q, pe = dev_bf16(inp.q_nope), dev_bf16(inp.q_pe)
+            qt = None if od == BF16 else torch.tensor([qs_val], dtype=torch.float32, device="cuda")
+            dt = torch.bfloat16 if od == BF16 else torch.uint8
+            canary = 0x5A5A if od == BF16 else 0x5A
+            outs = []
+            for hint in (mq.MLAQ_CACHE_DEFAULT, mq.MLAQ_CACHE_STREAM):
+                ws = torch.full((M, H, 640), canary, dtype=torch.int16 if od == BF16 else torch.uint8,
+                                device="cuda").view(dt)
+                mq.mlaq_run_ex(q, pe, w, s, qt, ws[:, :, :mq.ROW], wf, od, cache_hint=hint)
+                outs.append(ws)
+            torch.cuda.synchronize()
+            tag = f"stream hint wf={wf} od={od} K={K} H={H} M={M}"
+            assert torch.equal(outs[0], outs[1]), tag + ": differs from the default hint"
+            got = out_bits(outs[1][:, :, :mq.ROW].contiguous())
+            if od == BF16:
+                assert_bf16_parity(got, run_oracle(inp, od), tag)
+            else:
+                assert_e4m3_parity(got, run_oracle(inp, od, qs_val), tag)
+            pad = out_bits(outs[1][:, :, mq.ROW:].contiguous())
+            assert np.all(pad == canary), tag + ": pitch padding was written"
+
+
+def test_stream_hint_output_seen_by_the_next_kernel():
+    """The nontemporal stores of the streaming kernels are visible to the next
+    kernel on the stream: a graph of fused calls (BF16 weights, streaming
+    hint), each followed at once by a copy kernel reading the fresh output,
+    replayed with new inputs; every copy equals the oracle's result."""
+    H, M = 16, 32
+    first = inputs(SEED["c1"] + 11, H, WEIGHT_BF16, 128)
+    q, pe = dev_bf16(first.q_nope), dev_bf16(first.q_pe)
+    w, _ = weights(first)
+    qs = torch.tensor([0.02], dtype=torch.float32, device="cuda")
+    outs = [torch.empty((M, H, mq.ROW), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    seen = [torch.empty_like(o) for o in outs]
+    mq.mlaq_prewarm(H, [M], WEIGHT_BF16, E4M3)
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st, capture_error_mode="global"):
+            for o, s in zip(outs, seen):
+                mq.mlaq_run_ex(q, pe, w, None, qs, o, WEIGHT_BF16, E4M3, cache_hint=mq.MLAQ_CACHE_STREAM)
+                s.copy_(o)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate([SEED["c1"] + 12, SEED["c1"] + 13, SEED["c1"] + 12]):
+        cur = make_inputs(seed, H=H, weight_format=WEIGHT_BF16, M_draw=M)
+        q.copy_(dev_bf16(cur.q_nope))
+        pe.copy_(dev_bf16(cur.q_pe))
+        w.copy_(dev_bf16(cur.w))
+        for o, s in zip(outs, seen):
+            o.fill_(0xAA)
+            s.fill_(0x55)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = run_oracle(cur, E4M3, 0.02)
+        for i, s in enumerate(seen):
+            assert_e4m3_parity(out_bits(s), ref, f"replay {rep}, consumer copy {i}")
