@@ -144,6 +144,19 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int m) {
   return T < 0 ? 0 : (T > cap ? int(cap) : T);
 }
 
+// The logical block of this workgroup. Blocks are dealt round-robin over the
+// 8 XCDs (block b runs on XCD b % 8), each with its own L2. When the grid is a
+// multiple of 8, block b takes the logical index tile_of_block(b), so XCD x
+// holds a contiguous eighth of the logical blocks: at 32 sequences x 16 splits
+// the 16 split workgroups of a sequence share its query rows in one L2, and the
+// merge workgroups of that sequence (logical order sequence-major too) read the
+// partials from the L2 they were written to. Measured 1.2-1.4% shorter calls
+// (decode batch and 64k context) with bit-identical results.
+__device__ __forceinline__ int xcd_local_block() {
+  const int n = gridDim.x;
+  return (n & 7) == 0 ? dev::tile_of_block(blockIdx.x, n) : int(blockIdx.x);
+}
+
 template <int PD>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kvt[kTileBytes]; // the current tile, row = token
@@ -154,7 +167,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   const int S = a.S;
-  const int m = blockIdx.x / S, s = blockIdx.x - (blockIdx.x / S) * S;
+  const int bx = xcd_local_block();
+  const int m = bx / S, s = bx - (bx / S) * S;
   const int H = a.H;
   const int T = clamp_len(a, m);
   int ta, tb;
@@ -450,7 +464,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float part_sum[RG][kCols];
   __shared__ __attribute__((aligned(8))) float slice_sum[KS][kCols];
   const int H = a.H, S = a.S;
-  const int mh = blockIdx.x / QN, part = blockIdx.x - (blockIdx.x / QN) * QN;
+  const int bx = xcd_local_block();
+  const int mh = bx / QN, part = bx - (bx / QN) * QN;
   const int m = mh / H, h = mh - (mh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = tid % CG, rg = tid / CG;
