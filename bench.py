@@ -138,6 +138,40 @@ def step_graph(torch, mq, layers, wcopy, stream, cache_hint=None, only_wf=None):
     return g
 
 
+def graph_node_counts(torch, body):
+    """Nodes of a hipGraph captured from body() (a throwaway capture kept
+    un-instantiated), by type, read with hipGraphGetNodes / hipGraphNodeGetType
+    of the HIP runtime this process has loaded."""
+    import ctypes
+
+    path = next((line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line), None)
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph(keep_graph=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+            body()
+    torch.cuda.synchronize()
+    raw = ctypes.c_void_p(g.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    if hip.hipGraphGetNodes(raw, None, ctypes.byref(n)) != 0:
+        return None
+    nodes = (ctypes.c_void_p * n.value)()
+    if hip.hipGraphGetNodes(raw, nodes, ctypes.byref(n)) != 0:
+        return None
+    names = {0: "kernel", 1: "memcpy", 2: "memset"}
+    counts = {"nodes": int(n.value), "kernel": 0, "memcpy": 0, "memset": 0, "other": 0}
+    for nd in nodes:
+        t = ctypes.c_int(-1)
+        hip.hipGraphNodeGetType(ctypes.c_void_p(nd), ctypes.byref(t))
+        counts[names.get(t.value, "other")] += 1
+    del g
+    return counts
+
+
 def time_graphs(torch, graphs, steps, warmup, per_step_units=1):
     """hipEvent time of `steps` round-robin replays, ms per replay / unit."""
     for i in range(warmup):
@@ -226,13 +260,28 @@ def decode_step_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     staged_ms = time_graphs(torch, staged_graphs, args.steps, args.warmup)
     log(f"[bench] staged step: {staged_ms * 1e3:.2f} us/step ({staged_ms / ms:.2f}x fused)")
+
+    # Graph nodes per step (the pages compare kernel events per decode step).
+    def fused_body():
+        for L, (w, s) in zip(layers, copies[0]):
+            mq.mlaq_run_ex(L.q, L.pe, w, s, L.qs, L.out, L.wf, mq.MLAQ_OUT_E4M3, cache_hint=mq.MLAQ_CACHE_STREAM)
+
+    def staged_body():
+        for L, wb, ob in zip(layers, staged_w[0], tmp_out):
+            t = torch.bmm(L.q.transpose(0, 1).contiguous(), wb)
+            ob[..., :512].copy_(t.transpose(0, 1))
+            ob[..., 512:].copy_(L.pe)
+            L.out.view(torch.float8_e4m3fn).copy_((ob.float() / L.qs).clamp(-448.0, 448.0))
+
+    nodes = {"fused": graph_node_counts(torch, fused_body), "staged": graph_node_counts(torch, staged_body)}
+    log(f"[bench] graph nodes per step: fused {nodes['fused']}, staged {nodes['staged']}")
     del staged_graphs, staged_w, tmp_out, wbf
     torch.cuda.synchronize()
     floors = floors_leg(torch, mq, layers, copies, stream, args)
     return {
         "layers": layers, "ms": ms, "ms_default_hint": ms_default, "step_bytes": step_bytes, "dom_ms": dom_ms,
         "dom_ms_default_hint": dom[mq.MLAQ_CACHE_DEFAULT], "dom_bytes": dom_bytes,
-        "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes, "floors": floors,
+        "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes, "floors": floors, "nodes": nodes,
     }
 
 
@@ -369,6 +418,20 @@ def pages_shape_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     f_us = time_graphs(torch, fg, args.steps, args.warmup, per_step_units=L) * 1e3
     s_us = time_graphs(torch, sg, args.steps, args.warmup, per_step_units=L) * 1e3
+
+    def fused_body():
+        for d, w in zip(lay, wc[0]):
+            mq.mlaq_run_ex(d["q_hm"].transpose(0, 1), d["pe"], w, None, None, d["out"],
+                           mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16, cache_hint=mq.MLAQ_CACHE_STREAM)
+
+    def staged_body():
+        for d, w in zip(lay, wc[0]):
+            t = torch.bmm(d["q_hm"], w)
+            d["out"][..., :512].copy_(t.transpose(0, 1))
+            d["out"][..., 512:].copy_(d["pe"])
+
+    nodes = {"fused": graph_node_counts(torch, fused_body), "staged": graph_node_counts(torch, staged_body)}
+    log(f"[bench] pages' shape graph nodes per 78-layer step: fused {nodes['fused']}, staged {nodes['staged']}")
     log(f"[bench] pages' shape (K=192, H=8, M=1, BF16, 78 layers, cold): fused {f_us:.3f} us/layer, "
         f"staged {s_us:.3f} us/layer")
     del fg, sg, wc
@@ -419,6 +482,7 @@ def pages_shape_leg(torch, mq, wl, args):
     return {"workload": "K=192 (GLM), H=8 (TP8), M=1, BF16 W and out, q_nope as a head-major [H,M,K] view, "
                         "78 layers per hipGraph, 4 rotated weight copies (cold)",
             "fused_us_per_layer": round(f_us, 4), "staged_us_per_layer": round(s_us, 4),
+            "graph_nodes_per_step": nodes,
             "pages_context_us_per_layer": {"fused": 2.880912, "staged": 4.047940,
                                            "hardware": "eight SM12x-class GPUs, averaged over ranks (not this GPU)"},
             "ab_ba_graph_replay": {"samples_per_shape": args.ab_samples, "shapes": ab}}
@@ -744,7 +808,8 @@ def main():
                      "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles, streaming hint>",
                      "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"],
                      "us_per_launch_default_hint": round(step["dom_ms_default_hint"] * 1e3, 4)},
-        "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3)},
+        "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3),
+                   "graph_nodes_per_step": step["nodes"]["staged"], "fused_graph_nodes_per_step": step["nodes"]["fused"]},
         "floors": step["floors"],
         "per_call": per_call,
         "pages_shape": pages,
