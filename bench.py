@@ -23,7 +23,8 @@ Printed JSON line (stdout, one line):
               launch duration, timed live with hipEvents over back-to-back
               cold launches, against the 8 TB/s HBM peak
   per_call    warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
-              MXFP8 weights (BF16 output), with the staged torch baseline
+              MXFP8 weights (BF16 output), plus H=8 M=1 and H=11 M in
+              {1,3,7,16,32} (BF16), with the staged torch baseline
   pages_shape the pages' own workload (K=192, H=8, M=1, BF16, 78 layers,
               cold) fused vs staged per layer, and their AB/BA graph-replay
               comparison over H=8/11/16 x M=1/4/32
@@ -76,7 +77,7 @@ def parse():
     p.add_argument("--no-uv", action="store_true")
     p.add_argument("--no-attention", action="store_true")
     p.add_argument("--no-layer", action="store_true")
-    p.add_argument("--only", choices=["attention", "uv", "layer", "pages"],
+    p.add_argument("--only", choices=["attention", "uv", "layer", "pages", "percall"],
                    help="run only this leg and print its JSON (for profiling; no bench line)")
     p.add_argument("--ab-samples", type=int, default=1000, help="AB/BA samples per shape (pages' method)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-baseline sample")
@@ -332,14 +333,23 @@ def floors_leg(torch, mq, layers, copies, stream, args):
 
 
 def per_call_leg(torch, mq, wl, reps=100, replays=20):
+    """Warm-cache us per call: R = 100 back-to-back calls on the same buffers
+    in one hipGraph (BF16 output, default cache hint), against the staged
+    bmm + concat in the same harness. H = 16 with BF16 and MXFP8 weights over
+    M = 1..32 (the metric), plus the smallest case (H = 8, M = 1) and the odd
+    head count (H = 11, M = 1/3/7/16/32)."""
     res = {}
-    for name, wf, seed in (("bf16", mq.MLAQ_WEIGHT_BF16, wl.SEED["c1"]), ("mxfp8", mq.MLAQ_WEIGHT_MXFP8, wl.SEED["c3"])):
-        inp = wl.make_inputs(seed, H=H, weight_format=wf, M_draw=32)
+    cases = (("bf16", 16, mq.MLAQ_WEIGHT_BF16, wl.SEED["c1"], (1, 2, 4, 8, 16, 32)),
+             ("mxfp8", 16, mq.MLAQ_WEIGHT_MXFP8, wl.SEED["c3"], (1, 2, 4, 8, 16, 32)),
+             ("h8_bf16", 8, mq.MLAQ_WEIGHT_BF16, wl.SEED["c0"], (1,)),
+             ("h11_bf16", 11, mq.MLAQ_WEIGHT_BF16, wl.SEED["c2"], (1, 3, 7, 16, 32)))
+    for name, H, wf, seed, Ms in cases:
+        inp = wl.make_inputs(seed, H=H, weight_format=wf, M_draw=max(Ms))
         w = dev_bf16(torch, inp.w) if wf == mq.MLAQ_WEIGHT_BF16 else dev_u8(torch, inp.w)
         s = None if wf == mq.MLAQ_WEIGHT_BF16 else dev_u8(torch, inp.w_scales)
         wb = w if s is None else dequant_bf16(torch, w, s)
         rows = {}
-        for M in (1, 2, 4, 8, 16, 32):
+        for M in Ms:
             q = dev_bf16(torch, inp.q_nope[:M])
             pe = dev_bf16(torch, inp.q_pe[:M])
             out = torch.empty((M, H, mq.ROW), dtype=torch.bfloat16, device="cuda")
@@ -352,6 +362,8 @@ def per_call_leg(torch, mq, wl, reps=100, replays=20):
                     for _ in range(reps):
                         mq.mlaq_run(q, pe, w, s, None, out, wf, mq.MLAQ_OUT_BF16)
             us = time_graphs(torch, [g], replays, 3, per_step_units=reps) * 1e3
+            torch.bmm(q.transpose(0, 1).contiguous(), wb)  # the BLAS library initializes outside graph capture
+            torch.cuda.synchronize()
             gs = torch.cuda.CUDAGraph()
             with torch.cuda.stream(stream):
                 with torch.cuda.graph(gs, stream=stream):
@@ -363,7 +375,8 @@ def per_call_leg(torch, mq, wl, reps=100, replays=20):
             nbytes = wl.algorithmic_bytes(M, H, wf, mq.MLAQ_OUT_BF16)
             rows[str(M)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                             "staged_us": round(us_staged, 3)}
-            log(f"[bench] per-call {name} M={M}: {us:.3f} us ({rows[str(M)]['gbs']} GB/s), staged {us_staged:.3f} us")
+            log(f"[bench] per-call {name} H={H} M={M}: {us:.3f} us ({rows[str(M)]['gbs']} GB/s), "
+                f"staged {us_staged:.3f} us")
             del g, gs
         res[name] = rows
     return res
@@ -767,7 +780,8 @@ def main():
         return
     log(f"[bench] device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
     if args.only:
-        leg = {"attention": attention_leg, "uv": uv_leg, "layer": layer_leg, "pages": pages_shape_leg}[args.only]
+        leg = {"attention": attention_leg, "uv": uv_leg, "layer": layer_leg, "pages": pages_shape_leg,
+               "percall": lambda torch, mq, wl, args: per_call_leg(torch, mq, wl)}[args.only]
         print(json.dumps({args.only: leg(torch, mq, wl, args)}), flush=True)
         return
     step = decode_step_leg(torch, mq, wl, args)
