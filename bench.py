@@ -697,15 +697,20 @@ def cpu_baseline_leg(wl, layers, budget_s):
         inp = wl.make_inputs(wl.SEED["c4"] * 100 + idx, H=H, weight_format=wf, M_draw=M_STEP)
         qs = float(layers[idx].qs.item()) if layers is not None else 1.0
         host.append((wf, inp, qs))
-    done_bytes, t_used, n = 0, 0.0, 0
-    while t_used < budget_s:
-        wf, inp, qs = host[n % LAYERS]
-        t0 = time.perf_counter()
-        oracle.mla_query(inp.q_nope, inp.q_pe, inp.w, inp.w_scales, qs, weight_format=wf, out_dtype=1,
-                         threads=threads, diagnostics=False)
-        t_used += time.perf_counter() - t0
-        done_bytes += wl.algorithmic_bytes(M_STEP, H, wf, 1)
-        n += 1
+    def run(nthreads, budget):
+        done_bytes, t_used, n = 0, 0.0, 0
+        while t_used < budget:
+            wf, inp, qs = host[n % LAYERS]
+            t0 = time.perf_counter()
+            oracle.mla_query(inp.q_nope, inp.q_pe, inp.w, inp.w_scales, qs, weight_format=wf, out_dtype=1,
+                             threads=nthreads, diagnostics=False)
+            t_used += time.perf_counter() - t0
+            done_bytes += wl.algorithmic_bytes(M_STEP, H, wf, 1)
+            n += 1
+        return done_bytes, t_used, n
+
+    done_bytes, t_used, n = run(threads, budget_s)
+    one_bytes, one_t, one_n = run(1, max(1.0, budget_s / 4))
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -718,7 +723,9 @@ def cpu_baseline_leg(wl, layers, budget_s):
             "sample": f"{n} layer calls cycling over the {LAYERS} decode-step layers (H=16, M=32, E4M3 out, "
                       f"BF16/MXFP8 alternating), "
                       f"{t_used:.1f} s with {threads} threads on {cpu} (nproc {os.cpu_count()}); "
-                      f"{t_used / n * 1e3:.2f} ms per layer"}
+                      f"{t_used / n * 1e3:.2f} ms per layer",
+            "single_thread": {"value": round(one_bytes / one_t / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "ms_per_layer": round(one_t / one_n * 1e3, 2), "layer_calls": one_n}}
 
 
 def _recorded(name, sources, key):
@@ -793,7 +800,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_leg(wl, step["layers"], args.cpu_seconds)
-        log(f"[bench] cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+        log(f"[bench] cpu baseline: {cpu['value']} GB/s ({cpu['sample']}); 1 thread {cpu['single_thread']['value']} GB/s, "
+            f"{cpu['single_thread']['ms_per_layer']} ms per layer")
     ms = step["ms"]
     value = step["step_bytes"] / (ms * 1e-3) / 1e9
     dom_gbs = step["dom_bytes"] / (step["dom_ms"] * 1e-3) / 1e9
