@@ -78,18 +78,21 @@ __device__ __forceinline__ bool div_rn_covers(float b) {
   return ab >= 0x1p-90f && ab <= 0x1p126f;
 }
 
-// E8M0 scale byte -> 2^(s-127) as fp32 (0xff -> NaN).
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-  const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : s << 23);
-  return __uint_as_float(bits);
-}
+// E8M0 scale byte s as the scale operand of the scaled convert below: the
+// byte in the fp32 exponent field. The instruction reads only that field, so
+// this is the same operand as the exact value 2^(s-127) (with s = 0 as the
+// subnormal 2^-127 and s = 255 as NaN): an in-bounds probe gave identical
+// results for all 256 codes under all 256 scale bytes, one shift instead of
+// two compares and two selects per row.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t s) { return __uint_as_float(s << 23); }
 
 // Two E4M3 bytes of `word` (bytes 0-1, or 2-3 with hi) times `scale` as a
 // packed bf16 pair (low half = the lower byte), in one gfx950 instruction
-// (v_cvt_scalef32_pk_bf16_fp8). With scale = e8m0_scale(s) this is the exact
-// bf16 of every code's value times 2^(s-127) for s in 3..254 (checked bit for
-// bit against the fp32 conversion and product for all 256 codes and all 256
-// scale bytes); below that the result is a bf16 subnormal, rounded to nearest.
+// (v_cvt_scalef32_pk_bf16_fp8). With scale = e8m0_scale_operand(s) this is the
+// exact bf16 of every code's value times 2^(s-127) for s in 3..254 (checked
+// bit for bit against the fp32 conversion and product for all 256 codes and
+// all 256 scale bytes); below that the result is a bf16 subnormal, rounded to
+// nearest; s = 255 gives NaN.
 __device__ __forceinline__ uint32_t e4m3x2_scaled_bf16(uint32_t word, float scale, bool hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(word), scale, true)

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
       uint32_t wb[8][VEC / 2];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float s = e8m0_scale(sc[r]);
+        const float s = e8m0_scale_operand(sc[r]);
 #pragma unroll
         for (int e = 0; e < VEC; e += 2) wb[r][e >> 1] = e4m3x2_scaled_bf16(wr[r][e >> 2], s, (e >> 1) & 1);
       }

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
     if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
       // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16
       // pairs, one scaled conversion each.
-      const float s = e8m0_scale(sc[kb]);
+      const float s = e8m0_scale_operand(sc[kb]);
       u32x4_t d;
 #pragma unroll
       for (int p = 0; p < 4; ++p) d[p] = e4m3x2_scaled_bf16(b[p >> 1], s, p & 1);

@@ -198,6 +198,41 @@ def test_e4m3_decode_exhaustive():
     assert np.array_equal(gpu[~nan_ref], ref[~nan_ref])
 
 
+def test_e4m3_decode_every_scale_byte():
+    """Every E4M3 payload code under every scale byte of the exact domain
+    (10..246, where every nonzero decoded weight is a normal bf16 value) and
+    under 255 (NaN): the kernel passes the byte as the exponent field of the
+    scaled convert's fp32 operand. out[n] = bf16(decode(code) * 2^(S-127)) bit
+    for bit; byte 255 and the NaN codes give NaN. One byte per head, 16 heads
+    per call."""
+    H, M, k0 = 16, 1, 77
+    q = np.zeros((M, H, 128), np.uint16)
+    q[:, :, k0] = 0x3F80
+    pe = np.zeros((M, H, 64), np.uint16)
+    scale_bytes = list(range(10, 247)) + [255] * 2  # 239 bytes, then NaN heads to fill the last call
+    saw_nan_scale = False
+    for c0 in range(0, len(scale_bytes), H):
+        chunk = (scale_bytes[c0:c0 + H] + [255] * H)[:H]
+        w = np.zeros((H, 128, 512), np.uint8)
+        s = np.full((H, 128, 16), 127, np.uint8)
+        for h in range(H):
+            w[h, k0, :256] = np.arange(256, dtype=np.uint8)
+            w[h, k0, 256:] = np.arange(256, dtype=np.uint8)[::-1]
+            s[h, k0, :] = chunk[h]
+        inp = _Inp(q, pe, w, s, WEIGHT_MXFP8)
+        gpu = run_gpu(inp, BF16)
+        ref = run_oracle(inp, BF16)["out"]
+        nan_ref = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+        nan_gpu = ((gpu & 0x7F80) == 0x7F80) & ((gpu & 0x7F) != 0)
+        assert np.array_equal(nan_ref, nan_gpu), f"NaN pattern differs, scale bytes {chunk}"
+        assert np.array_equal(gpu[~nan_ref], ref[~nan_ref]), f"scale bytes {chunk}"
+        for h in range(H):
+            if chunk[h] == 255:
+                saw_nan_scale = True
+                assert nan_gpu[0, h, :512].all(), "scale byte 255 must give NaN"
+    assert saw_nan_scale
+
+
 @pytest.mark.parametrize("q_scale", [
     1.0, 0.125, 3.0, 1.0 / 448, -0.75,
     # The edges of the range where the kernel divides with one FMA correction
