@@ -211,6 +211,15 @@ int mlaq_uv_can_implement(int num_heads, int max_m, int latent_dim, int v_dim, i
 int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_format, int device);
 int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
                 int weight_format, void* stream);
+/*
+ * mlaq_uv_run with a cache hint (MLAQ_CACHE_*, as for mlaq_run_ex; timing
+ * only, results bit-identical; anything else is MLAQ_ERR_INVALID_ARG).
+ * MLAQ_CACHE_STREAM, for W_UV read once per decode step and cold in HBM,
+ * loads BF16 W_UV rows with the nontemporal hint; MXFP8 weights ignore it.
+ * mlaq_uv_run is this call with MLAQ_CACHE_DEFAULT.
+ */
+int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
+                   int weight_format, int cache_hint, void* stream);
 
 /*
  * Dense MLA decode attention with split partials, the consumer of the

@@ -114,6 +114,8 @@ def library() -> ctypes.CDLL:
         lib.mlaq_uv_prewarm.restype = I
         lib.mlaq_uv_run.argtypes = [P, P, P, P, I, I, I, P]
         lib.mlaq_uv_run.restype = I
+        lib.mlaq_uv_run_ex.argtypes = [P, P, P, P, I, I, I, I, P]
+        lib.mlaq_uv_run_ex.restype = I
         lib.mlaq_attn_workspace_size.argtypes = [I, I, I, I]
         lib.mlaq_attn_workspace_size.restype = ctypes.c_size_t
         lib.mlaq_attn_num_splits.argtypes = [I, I, I, ctypes.POINTER(I)]
@@ -300,11 +302,8 @@ def mlaq_uv_prewarm(num_heads: int, m_regimes, weight_format: int, device=None) 
     _check(library().mlaq_uv_prewarm(num_heads, arr, len(regs), weight_format, _device_index(device)))
 
 
-def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor | None, out: torch.Tensor,
-                weight_format: int, stream: torch.cuda.Stream | None = None) -> None:
-    """V up-projection: x bf16 [M,H,512], w_uv bf16 or float8_e4m3fn/uint8
-    [H,128,512] (latent contiguous), w_uv_scales uint8/float8_e8m0fnu
-    [H,128,16] (MXFP8) or None, out bf16 [M,H,128]."""
+def _uv_views(x, w_uv, w_uv_scales, out, weight_format):
+    """Checks of the UV arguments; returns (M, H)."""
     if x.dim() != 3:
         raise ValueError("x must be [M,H,512]")
     M, H = int(x.shape[0]), int(x.shape[1])
@@ -318,9 +317,30 @@ def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor |
                 w_uv_scales.dtype if w_uv_scales.dtype in (torch.uint8, torch.float8_e8m0fnu) else torch.uint8,
                 (H, V_DIM, LATENT_DIM // MX_BLOCK), dev)
     _expect(out, "out", torch.bfloat16, (M, H, V_DIM), dev)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return M, H
+
+
+def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor | None, out: torch.Tensor,
+                weight_format: int, stream: torch.cuda.Stream | None = None) -> None:
+    """V up-projection: x bf16 [M,H,512], w_uv bf16 or float8_e4m3fn/uint8
+    [H,128,512] (latent contiguous), w_uv_scales uint8/float8_e8m0fnu
+    [H,128,16] (MXFP8) or None, out bf16 [M,H,128]."""
+    M, H = _uv_views(x, w_uv, w_uv_scales, out, weight_format)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(library().mlaq_uv_run(_ptr(x), _ptr(w_uv), _ptr(w_uv_scales), _ptr(out), M, H, weight_format,
                                  ctypes.c_void_p(s.cuda_stream)))
+
+
+def mlaq_uv_run_ex(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor | None, out: torch.Tensor,
+                   weight_format: int, stream: torch.cuda.Stream | None = None,
+                   cache_hint: int = MLAQ_CACHE_DEFAULT) -> None:
+    """mlaq_uv_run with a cache hint: MLAQ_CACHE_STREAM when W_UV is read once
+    per decode step (cold in HBM), MLAQ_CACHE_DEFAULT otherwise; results are
+    identical."""
+    M, H = _uv_views(x, w_uv, w_uv_scales, out, weight_format)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    _check(library().mlaq_uv_run_ex(_ptr(x), _ptr(w_uv), _ptr(w_uv_scales), _ptr(out), M, H, weight_format,
+                                    cache_hint, ctypes.c_void_p(s.cuda_stream)))
 
 
 def mlaq_attn_workspace_size(M: int, H: int, num_splits: int, partial_dtype: int = MLAQ_PARTIAL_BF16) -> int:

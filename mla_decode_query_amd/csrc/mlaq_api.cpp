@@ -315,8 +315,11 @@ int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weig
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != device) e = hipSetDevice(device);
-    hipFuncAttributes attr;
-    if (e == hipSuccess) e = hipFuncGetAttributes(&attr, mlaq::uv_kernel_for(weight_format, m_regimes[i] <= 16 ? 1 : 2));
+    for (bool stream : {false, true}) {
+      const void* fn = mlaq::uv_kernel_for(weight_format, m_regimes[i] <= 16 ? 1 : 2, stream);
+      hipFuncAttributes attr;
+      if (e == hipSuccess && fn) e = hipFuncGetAttributes(&attr, fn);
+    }
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
   }
@@ -325,8 +328,15 @@ int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weig
 
 int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H, int weight_format,
                 void* stream) {
+  return mlaq_uv_run_ex(x, w_uv, w_uv_scales, out, M, H, weight_format, MLAQ_CACHE_DEFAULT, stream);
+}
+
+int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
+                   int weight_format, int cache_hint, void* stream) {
   clear_error();
   if (!known_weight_format(weight_format)) return fail(MLAQ_ERR_INVALID_ARG, "unknown weight_format %d", weight_format);
+  if (cache_hint != MLAQ_CACHE_DEFAULT && cache_hint != MLAQ_CACHE_STREAM)
+    return fail(MLAQ_ERR_INVALID_ARG, "unknown cache_hint %d", cache_hint);
   if (!supported_heads(H)) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d not in {8, 11, 16}", H);
   if (M < 0 || M > MLAQ_MAX_M) return fail(MLAQ_ERR_UNSUPPORTED, "M=%d outside 0..32", M);
   if (M == 0) return MLAQ_OK;
@@ -352,7 +362,8 @@ int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* 
   st = mlaq_uv_plan_supported(H, M, MLAQ_LATENT_DIM, MLAQ_V_DIM, weight_format, arch);
   if (st != MLAQ_OK) return st;
   const int m_tiles = M <= 16 ? 1 : 2;
-  const void* fn = mlaq::uv_kernel_for(weight_format, m_tiles);
+  const bool nt = cache_hint == MLAQ_CACHE_STREAM && weight_format == MLAQ_WEIGHT_BF16;
+  const void* fn = mlaq::uv_kernel_for(weight_format, m_tiles, nt);
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
   mlaq::uv_launch_shape(H, m_tiles, &grid, &block);

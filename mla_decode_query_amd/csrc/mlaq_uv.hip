@@ -40,12 +40,17 @@ using namespace dev;
 constexpr int kUvThreads = 256; // 4 waves
 constexpr int kUvScalesPerRow = kLatent / kMxBlock;
 
-template <int WF, int NMT, int CB>
+// NT (MLAQ_CACHE_STREAM, BF16 weights only): the W_UV rows are loaded with
+// the nontemporal hint. Same-box A/B, cold back-to-back layers: 3% shorter
+// BF16 launches (bit-identical), 7.5% longer back-to-back calls on one warm
+// weight set; nontemporal output stores and MXFP8 rows gained nothing.
+template <int WF, int NMT, int CB, bool NT>
 __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   constexpr int NVB = kValue / CB; // column blocks per head
   constexpr int MROWS = 16;        // tokens per workgroup
   constexpr int LDW = CB + 4;
   static_assert(CB == 8 || CB == 16, "8 or 16 value columns per workgroup");
+  static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 W_UV rows are streamed nontemporally");
   __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
 
   const int tid = threadIdx.x;
@@ -66,7 +71,12 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   if constexpr (WF == MLAQ_WEIGHT_BF16) {
     const uint32_t off = ((uint32_t(h) * kValue + v) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) wb[kb] = *at_byte<const u32x4_t>(a.w, off + 64 * kb);
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (NT)
+        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 64 * kb));
+      else
+        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 64 * kb);
+    }
   } else {
     u32x2_t w8[4];
     const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
@@ -135,16 +145,20 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
 // workgroups at H = 16 either way).
 constexpr int uv_cols(int m_tiles) { return m_tiles == 1 ? 8 : 16; }
 
-template <int WF, int NMT>
+template <int WF, int NMT, bool NT = false>
 const void* uv_kernel_ptr() {
-  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, NMT, uv_cols(NMT)>);
+  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, NMT, uv_cols(NMT), NT>);
 }
 
 } // namespace
 
-const void* uv_kernel_for(int weight_format, int m_tiles) {
-  if (weight_format == MLAQ_WEIGHT_BF16) return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2>();
-  if (weight_format == MLAQ_WEIGHT_MXFP8)
+const void* uv_kernel_for(int weight_format, int m_tiles, bool stream) {
+  if (weight_format == MLAQ_WEIGHT_BF16) {
+    if (stream)
+      return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1, true>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2, true>();
+    return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2>();
+  }
+  if (weight_format == MLAQ_WEIGHT_MXFP8 && !stream)
     return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 2>();
   return nullptr;
 }

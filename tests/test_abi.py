@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"mlaq_plan_supported", "mlaq_can_implement", "mlaq_prewarm",
                                          "mlaq_run", "mlaq_run_ex", "mlaq_last_error", "mlaq_uv_plan_supported",
                                          "mlaq_uv_can_implement", "mlaq_uv_prewarm", "mlaq_uv_run",
-                                         "mlaq_attn_workspace_size", "mlaq_attn_num_splits",
+                                         "mlaq_uv_run_ex", "mlaq_attn_workspace_size", "mlaq_attn_num_splits",
                                          "mlaq_attn_plan_supported", "mlaq_attn_can_implement", "mlaq_attn_prewarm",
                                          "mlaq_attn_run"}
 
@@ -267,6 +267,23 @@ def test_uv_run_rejects_before_any_device_call(lib, kw, status, msg):
 
 def test_uv_empty_batch_is_a_noop(lib):
     assert uv_run(lib, x=None, w=None, out=None, M=0) == OK
+
+
+@pytest.mark.parametrize("hint", [2, -1, 7])
+def test_uv_run_ex_rejects_unknown_cache_hint(lib, hint):
+    v = ctypes.c_void_p
+    assert lib.mlaq_uv_run_ex(v(A), v(2 * A), None, v(4 * A), 4, 16, 0, hint, None) == INV
+    assert f"cache_hint {hint}" in mq.mlaq_last_error()
+
+
+def test_uv_run_ex_default_hint_matches_uv_run_checks(lib):
+    """Both entry points reject the same bad plan the same way (the hint is
+    checked after the weight format, before anything else)."""
+    v = ctypes.c_void_p
+    for hint in (0, 1):
+        assert lib.mlaq_uv_run_ex(v(A), v(2 * A), None, v(2 * A + 256), 4, 16, 0, hint, None) == INV
+        assert "overlaps" in mq.mlaq_last_error()
+        assert lib.mlaq_uv_run_ex(None, None, None, None, 0, 16, 0, hint, None) == OK
 
 
 # --------------------------------------------------------------------------

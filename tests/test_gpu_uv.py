@@ -143,3 +143,30 @@ def test_uv_can_implement_on_device():
     assert mq.mlaq_uv_can_implement(16, 32, weight_format=WEIGHT_MXFP8)
     assert mq.mlaq_uv_can_implement(11, 1, weight_format=WEIGHT_BF16)
     assert not mq.mlaq_uv_can_implement(16, 32, v_dim=64)
+
+
+@pytest.mark.parametrize("wf", [WEIGHT_BF16, WEIGHT_MXFP8])
+def test_uv_stream_cache_hint(wf):
+    """mlaq_uv_run_ex with MLAQ_CACHE_STREAM (nontemporal BF16 W_UV loads; the
+    ordinary kernel for MXFP8) gives the oracle's parity and the bits of the
+    default hint for every head count and both token tiles, and leaves the
+    bytes past the output untouched."""
+    for H in (8, 11, 16):
+        x_all, w, s = uv_inputs(5100 + 10 * H + wf, H, wf)
+        wd = dev_bf16(w) if wf == WEIGHT_BF16 else dev_u8(w)
+        sd = None if s is None else dev_u8(s)
+        for M in (1, 9, 17, 32):
+            x = x_all[:M].copy()
+            xd = dev_bf16(x)
+            outs = []
+            for hint in (mq.MLAQ_CACHE_DEFAULT, mq.MLAQ_CACHE_STREAM):
+                buf = torch.full((M * H * 128 + 64,), 0x5A5A, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+                out = buf[:M * H * 128].view(M, H, 128)
+                mq.mlaq_uv_run_ex(xd, wd, sd, out, wf, cache_hint=hint)
+                outs.append(buf)
+            torch.cuda.synchronize()
+            tag = f"uv stream hint wf={wf} H={H} M={M}"
+            assert torch.equal(outs[0], outs[1]), tag + ": differs from the default hint"
+            got = out_bits(outs[1][:M * H * 128].view(M, H, 128))
+            assert_uv_parity(got, oracle.uv_projection(x, w, s, weight_format=wf), tag)
+            assert np.all(out_bits(outs[1][M * H * 128:]) == 0x5A5A), tag + ": wrote past the output"
