@@ -203,6 +203,8 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream);
  * All 16-byte aligned; out must not overlap an input. Sizes: latent 512,
  * value 128, H in {8, 11, 16}, M in 0..32 (0: no-op). Same status codes,
  * asynchrony, graph-capturability and determinism as mlaq_run.
+ * mlaq_uv_prewarm loads the kernels of the listed token counts for both
+ * cache hints (see mlaq_uv_run_ex).
  */
 int mlaq_uv_plan_supported(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format,
                            const char* arch);
