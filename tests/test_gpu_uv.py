@@ -170,3 +170,37 @@ def test_uv_stream_cache_hint(wf):
             got = out_bits(outs[1][:M * H * 128].view(M, H, 128))
             assert_uv_parity(got, oracle.uv_projection(x, w, s, weight_format=wf), tag)
             assert np.all(out_bits(outs[1][M * H * 128:]) == 0x5A5A), tag + ": wrote past the output"
+
+
+def test_uv_stream_hint_in_a_graph_with_a_consumer():
+    """Two streaming-hint UV calls captured in one graph, each followed at once
+    by a copy kernel reading its output; replays with new x and W_UV in place
+    match the oracle in every copy."""
+    H, M, wf = 11, 32, WEIGHT_BF16
+    mq.mlaq_uv_prewarm(H, [M], wf)
+    x0, w0, _ = uv_inputs(7100, H, wf, M=M)
+    xd, wd = dev_bf16(x0), dev_bf16(w0)
+    outs = [torch.empty((M, H, 128), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    seen = [torch.empty_like(o) for o in outs]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st, capture_error_mode="global"):
+            for o, s in zip(outs, seen):
+                mq.mlaq_uv_run_ex(xd, wd, None, o, wf, cache_hint=mq.MLAQ_CACHE_STREAM)
+                s.copy_(o)
+    torch.cuda.synchronize()
+    for seed in (7101, 7102, 7101):
+        x, w, _ = uv_inputs(seed, H, wf, M=M)
+        xd.copy_(dev_bf16(x))
+        wd.copy_(dev_bf16(w))
+        for o, s in zip(outs, seen):
+            o.zero_()
+            s.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.uv_projection(x, w)
+        for i, s in enumerate(seen):
+            assert_uv_parity(out_bits(s), ref, f"replay {seed}, consumer copy {i}")
