@@ -96,3 +96,15 @@ def test_recorded_traffic_follows_the_sources(name, sources, key, tmp_path, monk
     assert bench._recorded(name, sources, key) == int(kv[key])
     (csrc / sources[0]).write_bytes((csrc / sources[0]).read_bytes() + b"\n// edited\n")
     assert bench._recorded(name, sources, key) is None
+
+
+def test_cpu_baseline_object_on_a_tiny_budget():
+    """The cpu_baseline object the bench line carries: the oracle as it stands,
+    timed on the host over the step's layers (a budget small enough for the
+    CPU suite), with its thread count, and a single-thread figure beside it."""
+    r = bench.cpu_baseline_leg(wl, None, 0.05)
+    assert {"value", "unit", "cores", "kind", "sample", "single_thread"} <= set(r)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= 16 and f"{r['cores']} threads" in r["sample"]
+    one = r["single_thread"]
+    assert one["cores"] == 1 and one["value"] > 0 and one["layer_calls"] >= 1
