@@ -328,13 +328,48 @@ def check_invariants(lib=None):
     assert np.all(np.abs(base["acc"] - base["ref64"]) <= 2 * GAMMA_128 * base["s_abs"])
 
 
+def _bf16_scalar(x):
+    return int(bf16_bits(np.array([x], np.float32))[0])
+
+
 def check_qscale(lib=None):
+    """q_scale = amax / 448 over the layer's fp32 result: |projection accumulator|
+    (before bf16 rounding) and |q_pe|, 1 when that is zero. The expected values
+    below are exact quotients chosen so each one fails a different mistake."""
+    q = lambda a, pe: oracle.qscale_from_result(np.asarray(a, np.float32), np.asarray(pe, np.uint16), lib_path=lib)
     rng = _rng(41)
+    small = rng.uniform(-1.0, 1.0, (2, 16, N_LATENT)).astype(np.float32)
+    pe_small = bf16_bits(rng.uniform(-1.0, 1.0, (2, 16, R_ROPE)).astype(np.float32))
+    # The largest magnitude is a negative accumulator: 7 / 448 = 2^-6.
+    acc = small.copy()
+    acc[1, 5, 300] = -7.0
+    assert q(acc, pe_small) == 2.0 ** -6, "amax must be taken over |acc|, negative values included"
+    # The largest magnitude is a negative q_pe element: 14 / 448 = 2^-5.
+    pe = pe_small.copy()
+    pe[0, 9, 17] = _bf16_scalar(-14.0)
+    assert q(small, pe) == 2.0 ** -5, "amax must include |q_pe|"
+    pe[0, 9, 17] = _bf16_scalar(14.0)
+    assert q(small, pe) == 2.0 ** -5
+    # Projection all zero, q_pe not: 28 / 448 = 2^-4.
+    pe = np.zeros_like(pe_small)
+    pe[1, 0, 63] = _bf16_scalar(-28.0)
+    assert q(np.zeros_like(small), pe) == 2.0 ** -4
+    # q_pe all zero: the projection alone decides (a positive maximum, 896 / 448 = 2).
+    acc = small.copy()
+    acc[0, 0, 0] = 896.0
+    assert q(acc, np.zeros_like(pe_small)) == 2.0
+    # The fp32 accumulator, not its bf16 rounding: amax = 448 (1 + 2^-20) gives
+    # 1 + 2^-20 exactly, where the bf16 value would give 1.
+    acc = small.copy()
+    acc[1, 15, 511] = np.float32(448.0 * (1.0 + 2.0 ** -20))
+    assert q(acc, pe_small) == np.float32(1.0 + 2.0 ** -20), "amax must use the fp32 result before bf16"
+    # Everything zero: 1 (not 0, which would divide by zero downstream).
+    assert q(np.zeros_like(small), np.zeros_like(pe_small)) == 1.0
+    # Random data at the step's scale: the fp32 quotient of the largest magnitude.
     acc = (rng.standard_normal((4, 16, N_LATENT)) * 3).astype(np.float32)
     pe = _rand_bf16(rng, (4, 16, R_ROPE))
     amax = max(float(np.max(np.abs(acc))), float(np.max(np.abs(_f32(pe)))))
-    assert oracle.qscale_from_result(acc, pe, lib_path=lib) == np.float32(amax) / np.float32(448.0)
-    assert oracle.qscale_from_result(np.zeros_like(acc), np.zeros_like(pe), lib_path=lib) == 1.0
+    assert q(acc, pe) == np.float32(amax) / np.float32(448.0)
 
 
 ALL_CHECKS = [check_e4m3_decode, check_e8m0_decode, check_bf16_round, check_e4m3_encode,

@@ -45,6 +45,11 @@ MUTANTS = {
     "attn_last_range_short": ("b = a + chunk < T ? a + chunk : T;", "b = a + chunk < T ? a + chunk : T - 1;"),
     "f64_bf16_ties_up": ("r = fmod(lo, 2.0) == 0.0 ? lo * step : (lo + 1.0) * step;", "r = (lo + 1.0) * step;"),
     "f64_bf16_one_bit_short": ("int se = e - 8;", "int se = e - 7;"),
+    "qscale_ignores_q_pe": ("for (size_t i = 0; i < n_pe; ++i) {", "for (size_t i = 0; i < 0; ++i) {"),
+    "qscale_signed_acc": ("float a = fabsf(acc[i]);", "float a = acc[i];"),
+    "qscale_signed_q_pe": ("float a = fabsf(bf16_to_f32(q_pe[i]));", "float a = bf16_to_f32(q_pe[i]);"),
+    "qscale_no_zero_guard": ("return amax == 0.0f ? 1.0f : amax / 448.0f;", "return amax / 448.0f;"),
+    "qscale_divisor_480": ("return amax == 0.0f ? 1.0f : amax / 448.0f;", "return amax == 0.0f ? 1.0f : amax / 480.0f;"),
 }
 
 
