@@ -127,7 +127,10 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
  *
  * MXFP8 weights decode exactly for scale bytes 10..246, where every nonzero
  * decoded weight is a normal bf16 value (2^-126 <= |w| <= 448 * 2^119);
- * NaN payload codes propagate.
+ * NaN payload codes propagate, and scale byte 255 gives NaN. For bytes 0..9
+ * and 247..254 each weight is decoded to bf16 first: a weight in the bf16
+ * subnormal range is within one subnormal step (2^-133) of its exact value,
+ * one past the bf16 range is an infinity of its sign.
  * Results are deterministic: the same inputs give the same bits.
  * Returns MLAQ_OK, or a non-OK status with `out` untouched and nothing
  * enqueued; mlaq_last_error() describes it.
@@ -265,7 +268,10 @@ int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, voi
  * block_table_stride * page_size <= 2^30 tokens. M = 0 is a
  * no-op. Same status codes, asynchrony, graph-capturability and determinism
  * as mlaq_run; out, lse and workspace must not overlap the inputs or each
- * other.
+ * other. A non-OK status leaves out and lse untouched and enqueues nothing,
+ * with one exception: MLAQ_ERR_DEVICE from the merge launch of a call with
+ * num_splits > 1, when the split kernel (which writes only the workspace) has
+ * already been enqueued.
  */
 #define MLAQ_PARTIAL_BF16 0
 #define MLAQ_PARTIAL_FP32 1

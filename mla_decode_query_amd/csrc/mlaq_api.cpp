@@ -535,11 +535,21 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   const bool direct = a.num_splits == 1;
   int parts = 1, per_thread = 1;
   mlaq::attn_merge_shape(a.M, a.H, a.num_splits, &parts, &per_thread);
-  e = hipLaunchKernel(mlaq::attn_split_kernel_for(a.partial_dtype, direct), split_grid, block, kargs, 0, st_);
-  if (e == hipSuccess && !direct)
-    e = hipLaunchKernel(mlaq::attn_merge_kernel_for(a.partial_dtype, parts, per_thread), merge_grid, block, kargs, 0,
-                        st_);
-  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+  // Both kernels are resolved before the first launch, so a plan without a
+  // kernel fails with nothing enqueued.
+  const void* split_fn = mlaq::attn_split_kernel_for(a.partial_dtype, direct);
+  const void* merge_fn = direct ? nullptr : mlaq::attn_merge_kernel_for(a.partial_dtype, parts, per_thread);
+  if (!split_fn || (!direct && !merge_fn)) return fail(MLAQ_ERR_UNSUPPORTED, "no attention kernel for this plan");
+  e = hipLaunchKernel(split_fn, split_grid, block, kargs, 0, st_);
+  if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "split kernel launch: %s", hipGetErrorString(e));
+  if (!direct) {
+    // The split kernel of a multi-split call writes only the workspace, so a
+    // failed merge launch still leaves out and lse untouched.
+    e = hipLaunchKernel(merge_fn, merge_grid, block, kargs, 0, st_);
+    if (e != hipSuccess)
+      return fail(MLAQ_ERR_DEVICE, "merge kernel launch (the split kernel, which writes only the workspace, is "
+                                   "enqueued): %s", hipGetErrorString(e));
+  }
   return MLAQ_OK;
 }
 
