@@ -304,9 +304,39 @@ int mlaq_attn_num_splits(int M, int max_seq_len, int device, int* num_splits);
 int mlaq_attn_plan_supported(int num_heads, int page_size, int num_splits, int partial_dtype, const char* arch);
 int mlaq_attn_can_implement(int num_heads, int page_size, int num_splits, int partial_dtype, int device);
 /* Loads the split kernel of a partial dtype, every merge kernel shape it may
- * pair with, and the one-split kernel. */
+ * pair with, and the one-split kernel, and looks up the device address of the
+ * scratch array of mlaq_attn_run_noalloc on `device`. */
 int mlaq_attn_prewarm(int partial_dtype, int device);
 int mlaq_attn_run(const mlaq_attn_args* args, void* stream);
+
+/*
+ * Allocation-free form of mlaq_attn_run, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The same operation, kernels and results as
+ * mlaq_attn_run, with the partials and their lse kept in a library-owned
+ * device array of MLAQ_ATTN_SCRATCH_BYTES (one per device, created when the
+ * library's code object is loaded on it and held until the process ends)
+ * instead of a caller workspace:
+ *
+ *   args->workspace must be NULL and args->workspace_bytes 0
+ *   (else MLAQ_ERR_INVALID_ARG); plans whose
+ *   mlaq_attn_workspace_size(M, H, num_splits, partial_dtype) exceeds
+ *   MLAQ_ATTN_SCRATCH_BYTES are rejected with MLAQ_ERR_UNSUPPORTED (e.g.
+ *   32 sequences x 16 heads x 16 splits need 8.4 MB with BF16 partials and
+ *   16.8 MB with FP32 ones).
+ *
+ * No call allocates (no hipMalloc, hipFree or allocating library routine);
+ * the array's device address is looked up once per device, in
+ * mlaq_attn_prewarm or else in the first call on that device. All calls on
+ * one device share its array and it keeps the last call's contents; every
+ * call writes each partial before reading it, so nothing needs clearing.
+ * Calls that overlap in time on one device (different streams without an
+ * ordering between them) race on the array and give undefined results;
+ * calls ordered on one stream, or in one graph, are safe. Status codes and
+ * the rest of the contract are mlaq_attn_run's.
+ */
+#define MLAQ_ATTN_SCRATCH_BYTES (32u << 20)
+int mlaq_attn_run_noalloc(const mlaq_attn_args* args, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the thread's next mlaq_* call. */

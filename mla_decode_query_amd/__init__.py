@@ -51,6 +51,7 @@ MLAQ_ATTN_ROW = ROW
 MLAQ_ATTN_MAX_HEADS = 16
 MLAQ_ATTN_MAX_SPLITS = 256
 MLAQ_ATTN_SPLIT_ALIGN = 64
+MLAQ_ATTN_SCRATCH_BYTES = 32 << 20
 
 _STATUS_NAMES = {0: "MLAQ_OK", 1: "MLAQ_ERR_UNSUPPORTED", 2: "MLAQ_ERR_INVALID_ARG", 3: "MLAQ_ERR_DEVICE"}
 
@@ -128,6 +129,8 @@ def library() -> ctypes.CDLL:
         lib.mlaq_attn_prewarm.restype = I
         lib.mlaq_attn_run.argtypes = [ctypes.POINTER(AttnArgs), P]
         lib.mlaq_attn_run.restype = I
+        lib.mlaq_attn_run_noalloc.argtypes = [ctypes.POINTER(AttnArgs), P]
+        lib.mlaq_attn_run_noalloc.restype = I
         lib.mlaq_last_error.argtypes = []
         lib.mlaq_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -372,15 +375,8 @@ def mlaq_attn_prewarm(partial_dtype: int = MLAQ_PARTIAL_BF16, device=None) -> No
     _check(library().mlaq_attn_prewarm(partial_dtype, _device_index(device)))
 
 
-def mlaq_attn_run(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
-                  out: torch.Tensor, softmax_scale: float, num_splits: int,
-                  partial_dtype: int = MLAQ_PARTIAL_BF16, workspace: torch.Tensor | None = None,
-                  lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> None:
-    """Dense MLA decode attention: q bf16 [M,H,576] (a view whose last
-    dimension is contiguous), kv_cache bf16 [num_pages,page_size,576],
-    block_table int32 [M,max_blocks], seq_lens int32 [M], out bf16 [M,H,512],
-    lse fp32 [M,H] or None, workspace a uint8 tensor of at least
-    ``mlaq_attn_workspace_size`` bytes (None when that is 0)."""
+def _attn_args(q, kv_cache, block_table, seq_lens, out, softmax_scale, num_splits, partial_dtype, workspace,
+               lse) -> AttnArgs:
     if q.dim() != 3:
         raise ValueError("q must be [M,H,576]")
     M, H = int(q.shape[0]), int(q.shape[1])
@@ -402,12 +398,37 @@ def mlaq_attn_run(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
         if not workspace.is_contiguous() or workspace.device != dev:
             raise ValueError("workspace must be a contiguous tensor on the query's device")
         ws_bytes = workspace.numel() * workspace.element_size()
-    args = AttnArgs(q.data_ptr(), q_sm, q_sh, kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+    return AttnArgs(q.data_ptr(), q_sm, q_sh, kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
                     out.data_ptr(), None if lse is None else lse.data_ptr(),
                     None if workspace is None else workspace.data_ptr(), ws_bytes, float(softmax_scale),
                     M, H, page_size, num_pages, int(block_table.shape[1]), int(num_splits), int(partial_dtype))
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+
+
+def mlaq_attn_run(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                  out: torch.Tensor, softmax_scale: float, num_splits: int,
+                  partial_dtype: int = MLAQ_PARTIAL_BF16, workspace: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> None:
+    """Dense MLA decode attention: q bf16 [M,H,576] (a view whose last
+    dimension is contiguous), kv_cache bf16 [num_pages,page_size,576],
+    block_table int32 [M,max_blocks], seq_lens int32 [M], out bf16 [M,H,512],
+    lse fp32 [M,H] or None, workspace a uint8 tensor of at least
+    ``mlaq_attn_workspace_size`` bytes (None when that is 0)."""
+    args = _attn_args(q, kv_cache, block_table, seq_lens, out, softmax_scale, num_splits, partial_dtype, workspace,
+                      lse)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
     _check(library().mlaq_attn_run(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
+
+
+def mlaq_attn_run_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, out: torch.Tensor, softmax_scale: float, num_splits: int,
+                          partial_dtype: int = MLAQ_PARTIAL_BF16, lse: torch.Tensor | None = None,
+                          stream: torch.cuda.Stream | None = None) -> None:
+    """mlaq_attn_run with the partials in the library's device scratch array
+    (MLAQ_ATTN_SCRATCH_BYTES per device) instead of a caller workspace; for
+    callers that cannot allocate. Calls that overlap in time on one device race."""
+    args = _attn_args(q, kv_cache, block_table, seq_lens, out, softmax_scale, num_splits, partial_dtype, None, lse)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _check(library().mlaq_attn_run_noalloc(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
 
 
 def dense_mla_decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, num_splits: int | None = None,

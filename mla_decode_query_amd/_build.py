@@ -20,7 +20,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libmlaq.so"
-SOURCES = [CSRC / "mlaq_kernels.hip", CSRC / "mlaq_uv.hip", CSRC / "mlaq_attn.hip", CSRC / "mlaq_api.cpp"]
+SOURCES = [CSRC / "mlaq_kernels.hip", CSRC / "mlaq_uv.hip", CSRC / "mlaq_attn.hip", CSRC / "mlaq_scratch.hip",
+           CSRC / "mlaq_api.cpp"]
 # Measurement floors used by bench.py (not part of the fused path).
 DIAG_LIB = PKG / "libmlaq_diag.so"
 DIAG_SOURCES = [CSRC / "mlaq_diag.hip"]

@@ -445,15 +445,27 @@ int mlaq_attn_prewarm(int partial_dtype, int device) {
       hipFuncAttributes attr;
       if (e == hipSuccess) e = hipFuncGetAttributes(&attr, mlaq::attn_merge_kernel_for(partial_dtype, parts, r));
     }
+  void* scratch = nullptr; // the allocation-free entry point's array: address looked up once here
+  if (e == hipSuccess) e = mlaq::scratch_address(device, &scratch);
   if (cur != device) (void)hipSetDevice(cur);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading attention kernels: %s", hipGetErrorString(e));
   return MLAQ_OK;
 }
 
-int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
+} // extern "C"
+
+namespace {
+
+// mlaq_attn_run (use_scratch false: the caller's workspace) and
+// mlaq_attn_run_noalloc (use_scratch true: the library's device array, no
+// caller workspace). Every check that needs no HIP call comes first, so both
+// entry points report the same argument errors in the same order.
+int attn_run(const mlaq_attn_args* args, bool use_scratch, void* stream) {
   clear_error();
   if (!args) return fail(MLAQ_ERR_INVALID_ARG, "args is NULL");
   const mlaq_attn_args& a = *args;
+  if (use_scratch && (a.workspace || a.workspace_bytes))
+    return fail(MLAQ_ERR_INVALID_ARG, "mlaq_attn_run_noalloc takes no workspace (pass NULL and 0 bytes)");
   if (!known_partial(a.partial_dtype)) return fail(MLAQ_ERR_INVALID_ARG, "unknown partial_dtype %d", a.partial_dtype);
   if (a.H < 1 || a.H > mlaq::kAttnMaxHeads) return fail(MLAQ_ERR_UNSUPPORTED, "H=%d outside 1..16", a.H);
   if (a.page_size < 1 || a.page_size > mlaq::kAttnMaxPage)
@@ -477,9 +489,15 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   if (!aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.lse, 4))
     return fail(MLAQ_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
   const size_t ws = mlaq_attn_workspace_size(a.M, a.H, a.num_splits, a.partial_dtype);
-  if (ws > 0 && (!a.workspace || a.workspace_bytes < ws))
-    return fail(MLAQ_ERR_INVALID_ARG, "workspace must hold %zu bytes", ws);
-  if (ws > 0 && !aligned(a.workspace, 256)) return fail(MLAQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (use_scratch) {
+    if (ws > mlaq::kAttnScratchBytes)
+      return fail(MLAQ_ERR_UNSUPPORTED, "plan needs %zu bytes of scratch; the library's array holds %zu", ws,
+                  mlaq::kAttnScratchBytes);
+  } else {
+    if (ws > 0 && (!a.workspace || a.workspace_bytes < ws))
+      return fail(MLAQ_ERR_INVALID_ARG, "workspace must hold %zu bytes", ws);
+    if (ws > 0 && !aligned(a.workspace, 256)) return fail(MLAQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
   // Address spans: inputs and outputs must not overlap.
   const size_t mh = size_t(a.M) * size_t(a.H);
   const size_t q_bytes = size_t((int64_t(a.M) - 1) * a.q_stride_m + (int64_t(a.H) - 1) * a.q_stride_h + mlaq::kRow) * 2;
@@ -489,7 +507,7 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   const size_t out_bytes = mh * mlaq::kLatent * 2, lse_bytes = a.lse ? mh * 4 : 0;
   const void* ins[] = {a.q, a.kv_cache, a.block_table, a.seq_lens};
   const size_t in_bytes[] = {q_bytes, kv_bytes, bt_bytes, sl_bytes};
-  const void* outs[] = {a.out, a.lse, ws > 0 ? a.workspace : nullptr};
+  const void* outs[] = {a.out, a.lse, ws > 0 && !use_scratch ? a.workspace : nullptr};
   const size_t out_sizes[] = {out_bytes, lse_bytes, ws};
   for (int o = 0; o < 3; ++o) {
     for (int i = 0; i < 4; ++i)
@@ -507,14 +525,20 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   if (st != MLAQ_OK) return st;
   st = mlaq_attn_plan_supported(a.H, a.page_size, a.num_splits, a.partial_dtype, arch);
   if (st != MLAQ_OK) return st;
+  void* workspace = a.workspace;
+  if (use_scratch && ws > 0) {
+    e = mlaq::scratch_address(device, &workspace);
+    if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "scratch array address on device %d: %s", device,
+                                     hipGetErrorString(e));
+  }
 
   mlaq::AttnArgs ka{};
   ka.q = static_cast<const uint16_t*>(a.q);
   ka.kv = static_cast<const uint16_t*>(a.kv_cache);
   ka.bt = a.block_table;
   ka.seq_lens = a.seq_lens;
-  ka.part = ws > 0 ? a.workspace : nullptr;
-  ka.part_lse = ws > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) +
+  ka.part = ws > 0 ? workspace : nullptr;
+  ka.part_lse = ws > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                                  attn_lse_offset(a.M, a.H, a.num_splits, a.partial_dtype))
                        : nullptr;
   ka.out = static_cast<uint16_t*>(a.out);
@@ -552,6 +576,14 @@ int mlaq_attn_run(const mlaq_attn_args* args, void* stream) {
   }
   return MLAQ_OK;
 }
+
+} // namespace
+
+extern "C" {
+
+int mlaq_attn_run(const mlaq_attn_args* args, void* stream) { return attn_run(args, false, stream); }
+
+int mlaq_attn_run_noalloc(const mlaq_attn_args* args, void* stream) { return attn_run(args, true, stream); }
 
 const char* mlaq_last_error(void) { return g_err; }
 

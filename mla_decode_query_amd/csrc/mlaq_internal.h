@@ -73,6 +73,12 @@ constexpr int kAttnMaxSplits = 256;
 constexpr int kAttnMaxPage = 4096;  // tokens per cache page
 constexpr int kAttnMaxM = 65536;
 
+// Library-owned device scratch of mlaq_attn_run_noalloc (one per device,
+// held until the process ends): its size, and the device address of the
+// copy on `device` (looked up once per device with that device current).
+constexpr size_t kAttnScratchBytes = size_t(MLAQ_ATTN_SCRATCH_BYTES);
+hipError_t scratch_address(int device, void** ptr);
+
 struct AttnArgs {
   const uint16_t* q;        // bf16 [M,H,576] at (q_sm, q_sh, 1)
   const uint16_t* kv;       // bf16 [num_pages, P, 576], contiguous

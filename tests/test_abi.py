@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
                                          "mlaq_uv_can_implement", "mlaq_uv_prewarm", "mlaq_uv_run",
                                          "mlaq_uv_run_ex", "mlaq_attn_workspace_size", "mlaq_attn_num_splits",
                                          "mlaq_attn_plan_supported", "mlaq_attn_can_implement", "mlaq_attn_prewarm",
-                                         "mlaq_attn_run"}
+                                         "mlaq_attn_run", "mlaq_attn_run_noalloc"}
 
 
 def test_library_exports_every_declared_function(lib):
@@ -414,3 +414,46 @@ def test_attn_num_splits_rejects_before_device(lib):
     assert lib.mlaq_attn_num_splits(4, -1, 0, ctypes.byref(n)) == INV
     assert lib.mlaq_attn_num_splits(4, 100, 99, ctypes.byref(n)) == INV  # device ordinal out of range
     assert lib.mlaq_attn_prewarm(7, 0) == INV
+
+
+def attn_run_noalloc(lib, **kw):
+    # The same disjoint, never dereferenced pointers as attn_run, with no workspace.
+    M, H, S = 4, 16, 4
+    a = mq.AttnArgs(A, 16 * 576, 576, 64 * A, 2 * A, 3 * A, 4 * A, None, None, 0, 0.07, M, H, 64, 10, 8, S, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.mlaq_attn_run_noalloc(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(workspace=8 * A), INV, "takes no workspace"),
+    (dict(workspace_bytes=4096), INV, "takes no workspace"),
+    (dict(partial_dtype=5), INV, "partial_dtype"),
+    (dict(H=17), UNS, "H=17"),
+    (dict(num_splits=300), UNS, "num_splits=300"),
+    (dict(q=None), INV, "non-NULL"),
+    (dict(q_stride_h=100), INV, "multiples of 8"),
+    (dict(out=64 * A + 4096), INV, "overlaps an input"),
+    # 4096 sequences x 16 heads x 64 splits of BF16 partials: 1 GiB, above the 32 MiB array.
+    (dict(M=4096, num_splits=64), UNS, "bytes of scratch"),
+    # FP32 partials of 32 x 16 x 64 splits: 67 MB.
+    (dict(M=32, num_splits=64, partial_dtype=1), UNS, "bytes of scratch"),
+])
+def test_attn_run_noalloc_rejects_before_any_device_call(lib, kw, status, msg):
+    assert attn_run_noalloc(lib, **kw) == status
+    assert msg in mq.mlaq_last_error()
+
+
+def test_attn_run_noalloc_null_args_and_empty_batch(lib):
+    assert lib.mlaq_attn_run_noalloc(None, None) == INV
+    assert attn_run_noalloc(lib, M=0, q=None, kv_cache=None, out=None) == OK
+    assert mq.mlaq_last_error() == ""
+
+
+def test_attn_scratch_limit_matches_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define MLAQ_ATTN_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mq.MLAQ_ATTN_SCRATCH_BYTES == 32 << 20
+    # The decode batch of the benchmark (32 sequences, 16 heads, 16 splits) fits in both partial dtypes.
+    assert mq.mlaq_attn_workspace_size(32, 16, 16, 1) <= mq.MLAQ_ATTN_SCRATCH_BYTES
+    assert mq.mlaq_attn_workspace_size(32, 16, 16, 0) <= mq.MLAQ_ATTN_SCRATCH_BYTES
