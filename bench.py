@@ -835,7 +835,7 @@ def main():
                       f"{step['ms_default_hint'] * 1e3:.2f} us",
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles, streaming hint>",
+                     "kernel": "fused_query_kernel<bf16 W, E4M3 out, 2 M-tiles, 4 waves, streaming hint, 32 columns>",
                      "us_per_launch": round(step["dom_ms"] * 1e3, 4), "bytes_per_launch": step["dom_bytes"],
                      "us_per_launch_default_hint": round(step["dom_ms_default_hint"] * 1e3, 4)},
         "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3),

@@ -34,6 +34,12 @@ HIPCC_FLAGS = [
     # MFMA accumulators in ordinary VGPRs (gfx90a+ form): saves the AGPR read-back
     # of every partial tile before the LDS reduction.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # Kernel-argument preloading (gfx950): the first 14 dwords of a kernel's
+    # scalar arguments arrive in SGPRs with the wave, so no wave waits for a
+    # kernel-argument load before its first memory request (the code object
+    # keeps a load-based entry for firmware without it). Kernels whose early
+    # arguments fit take scalar arguments, not a struct, for this.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
 ]
 

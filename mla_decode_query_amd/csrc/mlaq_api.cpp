@@ -174,7 +174,7 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
     st = plan_for(num_heads, m_regimes[i], MLAQ_NOPE_DIM, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, weight_format, out_dtype,
                   arch);
     if (st != MLAQ_OK) return st;
-    const int tiles = mlaq::variant_for(weight_format, out_dtype, m_regimes[i], mlaq::kNope).m_tiles;
+    const int tiles = mlaq::variant_for(weight_format, out_dtype, m_regimes[i], mlaq::kNope, num_heads).m_tiles;
     if (seen[tiles]) continue;
     seen[tiles] = true;
     int cur = 0;
@@ -185,7 +185,8 @@ int mlaq_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weight_
         hipFuncAttributes attr;
         if (e == hipSuccess)
           e = hipFuncGetAttributes(&attr,
-                                   mlaq::kernel_for(mlaq::variant_for(weight_format, out_dtype, m_regimes[i], K, hint)));
+                                   mlaq::kernel_for(mlaq::variant_for(weight_format, out_dtype, m_regimes[i], K,
+                                                                      num_heads, hint)));
       }
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
@@ -244,7 +245,7 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   st = plan_for(H, M, K, MLAQ_LATENT_DIM, MLAQ_ROPE_DIM, a.weight_format, a.out_dtype, arch);
   if (st != MLAQ_OK) return st;
 
-  const mlaq::Variant v = mlaq::variant_for(a.weight_format, a.out_dtype, M, K, a.cache_hint);
+  const mlaq::Variant v = mlaq::variant_for(a.weight_format, a.out_dtype, M, K, H, a.cache_hint);
   const void* fn = mlaq::kernel_for(v);
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
@@ -253,7 +254,8 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
                      static_cast<const uint8_t*>(a.w_scales), a.q_scale, a.out,
                      uint32_t(a.q_stride_m), uint32_t(a.q_stride_h), uint32_t(a.pe_stride_m),
                      uint32_t(a.pe_stride_h), uint32_t(a.out_stride_m), uint32_t(a.out_stride_h), M, H};
-  void* kargs[] = {&ka};
+  void* kargs[] = {&ka.q_pe, &ka.w, &ka.q_nope, &ka.w_scales, &ka.pe_sm, &ka.pe_sh, &ka.q_sm,
+                   &ka.q_sh, &ka.M, &ka.H, &ka.out, &ka.q_scale, &ka.out_sm, &ka.out_sh};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;
@@ -368,7 +370,7 @@ int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, voi
   dim3 grid, block;
   mlaq::uv_launch_shape(H, m_tiles, &grid, &block);
   mlaq::UvArgs ka{static_cast<const uint16_t*>(x), w_uv, static_cast<const uint8_t*>(w_uv_scales), out, M, H};
-  void* kargs[] = {&ka};
+  void* kargs[] = {&ka.x, &ka.w, &ka.w_scales, &ka.out, &ka.M, &ka.H};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;

@@ -77,14 +77,6 @@ constexpr int kPartialFp32 = MLAQ_PARTIAL_FP32;
 constexpr int kDirect = 2; // one split: write the final output
 constexpr int kMergeMaxR = 8;  // most ranges per merge thread (all requested at once)
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-// An LDS byte pointer as the operand type of the transpose read.
-__device__ __forceinline__ __attribute__((address_space(3))) v4i16_t* lds_v4i16(const uint8_t* p) {
-  return (__attribute__((address_space(3))) v4i16_t*)(
-      (__attribute__((address_space(3))) uint8_t*)(const_cast<uint8_t*>(p)));
-}
-
 // DPP lane exchange within rows of 16 lanes (float payload).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -18,7 +18,16 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
 constexpr int kScalesPerRow = kLatent / kMxBlock;
+
+// An LDS byte pointer as the operand type of the gfx950 transpose read
+// (__builtin_amdgcn_ds_read_tr16_b64_v4i16, ds_read_b64_tr_b16).
+__device__ __forceinline__ __attribute__((address_space(3))) v4i16_t* lds_v4i16(const uint8_t* p) {
+  return (__attribute__((address_space(3))) v4i16_t*)(
+      (__attribute__((address_space(3))) uint8_t*)(const_cast<uint8_t*>(p)));
+}
 
 // ---------------------------------------------------------------------------
 // Conversions. bf16 and E4M3 encodes use the gfx950 convert instructions,

@@ -12,20 +12,26 @@
 // kernel is an HBM stream whose cost is latency: every weight byte is
 // requested at kernel entry, spread over as many CUs as the tiling allows.
 // A workgroup of K/32 waves (4 for K = 128, 6 for K = 192) owns one head h
-// and one slice of WCOLS = 16*VEC latent columns, over all K. Wave w takes k
-// rows [32w, 32w+32).
+// and one tile of WC latent columns (WC = 32: 16 workgroups per head), over
+// all K. Wave w takes k rows [32w, 32w+32).
 //
-// Contraction on MFMA without any transpose. v_mfma_f32_16x16x32_bf16 pairs
-// element e of lane (i + 16g) of A with element e of lane (j + 16g) of B, for
-// output (i, j). A lane loads VEC consecutive columns of 8 consecutive k rows
-// (the weight is n-major, so each row segment is a coalesced load). For each
-// of its VEC columns it builds a B fragment from those 8 rows (v_perm packs
-// two rows' bf16 into one dword) and issues one MFMA whose output column j is
-// relabelled as latent column c0 + VEC*j + i. The A fragment is the q_nope
-// row of token i over the same 8 k per lane group, loaded straight from
-// global memory. So the 16-wide MFMA column index walks 16 column groups, the
-// 4 lane groups walk the 4 k octets, and no LDS round trip is needed for
-// either operand. M <= 16 uses one 16-token tile, M <= 32 two.
+// Loads. Each lane requests pieces of whole weight rows of up to 16 bytes
+// (the weight is n-major, so a tile's row segment is contiguous): one load
+// instruction covers 16 (BF16) or 32 (E4M3) whole row segments, and an MXFP8
+// lane also loads the one E8M0 byte of its row and column group, 5 memory
+// requests per wave in all with q_pe and the q_nope fragments. The
+// arguments the first requests need are the kernel's first scalar
+// arguments, which arrive preloaded in SGPRs (no kernel-argument load on the
+// critical path).
+//
+// Contraction on MFMA. v_mfma_f32_16x16x32_bf16 pairs element e of lane
+// (i + 16g) of A with element e of lane (j + 16g) of B, for output (i, j):
+// A is q_nope of token i over 8 consecutive k (one 16-byte load straight
+// from global memory), B is the weight column j over the same 8 k. A wave
+// writes its 32 x WC bf16 tile (MXFP8 decoded first) to its own LDS slice
+// and reads the B fragments back with the gfx950 transpose read, so no
+// workgroup barrier separates the loads from the MFMAs. M <= 16 uses one
+// 16-token tile, M <= 32 two.
 //
 // The waves' fp32 partial tiles are summed through LDS in a fixed order
 // (wave 0 + 1 + 2 + ...), so results are deterministic. The epilogue rounds to
@@ -39,8 +45,8 @@
 // shortened the cold BF16-weight launch by 8-10% in same-box A/B runs
 // (identical output bits) and lengthened back-to-back calls on one cached
 // weight set by 5-14%, hence a caller's hint rather than the only form.
-// MXFP8 rows are 32-byte segments whose 128-byte lines four workgroups share;
-// there every nontemporal form was slower, so those kernels have no NT form.
+// A 128-byte line of MXFP8 rows is shared by four workgroups; there every
+// nontemporal form was slower, so those kernels have no NT form.
 //
 // MXFP8 weights are decoded in registers: v_cvt_scalef32_pk_bf16_fp8 turns
 // two E4M3 bytes and the 2^(S-127) scale into their exact bf16 values in one
@@ -70,60 +76,102 @@ struct Flag {
 };
 
 // ---------------------------------------------------------------------------
-// The fused kernel
+// The fused kernel. One workgroup per head and WC-column tile (WC = 32 or
+// 16; wave w owns k rows [32w, 32w+32)); each lane loads whole pieces of
+// weight rows, of up to 16 bytes: the
+// wave's 32 x WC tile is RBY = WC * (bytes per weight) bytes per row, every
+// lane takes RBY/2 of them (16 or 32 bytes for BF16, 8 or 16 for E4M3) in
+// loads of PB bytes, LPR lanes per row segment, so each load instruction
+// covers 64/LPR whole row segments. MXFP8 rows come with the one scale byte
+// of that row and column group, and are decoded to bf16 in registers. The
+// wave then writes its 32 x WC bf16 tile to its own LDS slice and reads the
+// MFMA B fragments back with the gfx950 transpose read (ds_read_b64_tr_b16):
+// within a 16-lane group, output lane i gets element i%4 of the 8 bytes that
+// lane 4e + i/4 points at, so lane 4e + q points at columns 4q..4q+3 of k row
+// 8g + e (and 8g + 4 + e for the second read), and lane (j, g) receives k rows
+// 8g..8g+7 of column j: exactly the B operand pairing with the q_nope A
+// fragment of the same k. Each wave reads only rows it wrote itself, so the
+// hand-off needs no workgroup barrier. Every output sums the same products in
+// the same MFMA positions whatever WC is, so the tile widths give identical
+// bits.
 // ---------------------------------------------------------------------------
 
-template <int WF, int OF, int MT, int VEC, int NW, bool NT>
-__global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
-  constexpr int K = 32 * NW;                            // reduction width
+template <int WF, int OF, int MT, int NW, bool NT, int WC>
+__global__ __launch_bounds__(64 * NW) void fused_query_kernel(
+    const uint16_t* q_pe, const void* w, const uint16_t* q_nope, const uint8_t* w_scales, uint32_t pe_sm,
+    uint32_t pe_sh, uint32_t q_sm, uint32_t q_sh, int M_, int H_, void* out, const float* q_scale, uint32_t out_sm,
+    uint32_t out_sh) {
+  // Scalar arguments, ordered so that everything the first loads need lies
+  // in the first 16 dwords of the kernel-argument segment: with kernel
+  // argument preloading those arrive in SGPRs with the wave, and no wave waits
+  // for a kernel-argument load before it can request its data.
+  const FusedArgs a{q_nope, q_pe, w, w_scales, q_scale, out, q_sm, q_sh, pe_sm, pe_sh, out_sm, out_sh, M_, H_};
+  constexpr int K = 32 * NW;
   constexpr int THREADS = 64 * NW;
-  constexpr int ESZ = (WF == MLAQ_WEIGHT_BF16) ? 2 : 1; // bytes per weight
-  constexpr int WCOLS = 16 * VEC;                       // latent columns per workgroup
-  constexpr int NCT = kLatent / WCOLS;                  // column tiles per head
-  constexpr int RB = VEC * ESZ;                         // bytes per lane per k row
-  constexpr int D = (RB + 3) / 4;                       // dwords per lane per k row
+  constexpr int NCT = kLatent / WC;
   constexpr int MROWS = 16 * MT;
-  constexpr int LDW = WCOLS + 4; // padded LDS row, in floats
-  static_assert(WF != MLAQ_WEIGHT_BF16 || VEC % 2 == 0, "bf16 columns come in dword pairs");
-  static_assert(WF != MLAQ_WEIGHT_MXFP8 || VEC % 2 == 0, "E4M3 columns are decoded in pairs");
+  constexpr int LDW = WC + 4;                           // padded partial-tile row, in floats
+  constexpr int TP = 2 * WC + 16;                       // weight-tile row pitch in bytes (bf16 + padding)
+  constexpr int ESZ = (WF == MLAQ_WEIGHT_BF16) ? 2 : 1; // bytes per weight in HBM
+  constexpr int RBY = WC * ESZ;                         // bytes per row segment
+  constexpr int PB = RBY / 2 < 16 ? RBY / 2 : 16;       // bytes per load
+  constexpr int NL = (RBY / 2) / PB;                    // loads per lane
+  constexpr int LPR = RBY / PB;                         // lanes per row segment
+  constexpr int RPL = 64 / LPR;                         // row segments per load
+  constexpr int PD = PB / 4;                            // dwords per load
+  constexpr int OD = PD * (2 / ESZ);                    // bf16 dwords per load
+  static_assert(WC == 16 || WC == 32, "tiles of 16 or 32 columns");
+  static_assert(PD == 2 || PD == 4, "8- or 16-byte pieces");
+  static_assert(WF == MLAQ_WEIGHT_BF16 || NL == 1, "one E4M3 piece (and scale byte) per lane");
   static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 weight rows are streamed nontemporally");
   __shared__ __attribute__((aligned(16))) float part[NW * MROWS * LDW];
+  __shared__ __attribute__((aligned(16))) uint8_t wtile[NW * 32 * TP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int tile = tile_of_block(blockIdx.x, a.H * NCT); // the grid is H x NCT workgroups
   const int h = tile / NCT, ct = tile - h * NCT;
-  const int c0 = ct * WCOLS;
+  const int c0 = ct * WC;
   const int M = a.M;
-  const int k0 = 32 * wave + 8 * g; // first of this lane's 8 k rows
-  const int col = c0 + VEC * j;     // first of this lane's VEC columns
+  const int k0 = 32 * wave + 8 * g;      // first k of this lane's A and B fragments
+  const int r0 = lane / LPR;             // wave-local row of this lane's first piece (+RPL per load)
+  const int pcol = (PB / ESZ) * (lane % LPR); // first tile column of each piece
 
   // 1. This thread's q_pe chunk (8 elements), requested first so that its
   //    store can leave while the weights are still in flight. Chunk x of the
   //    head goes to column tile x % NCT, thread x / NCT.
   const int pe_chunk = ct + NCT * tid;
   const bool has_pe = pe_chunk < M * (kRope / 8);
-  const int pe_x = has_pe ? pe_chunk : 0; // loads stay unconditional (no branch, no early wait)
+  const int pe_x = has_pe ? pe_chunk : 0;
   const int pe_m = pe_x >> 3, pe_c = pe_x & 7;
   const uint32_t pe_off = __umul24(pe_m, a.pe_sm) + __umul24(h, a.pe_sh) + 8 * pe_c;
   const u32x4_t pe_v = *at_byte<const u32x4_t>(a.q_pe, 2 * pe_off);
-  __builtin_amdgcn_sched_barrier(0); // keep the q_pe load ahead of the weight loads
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. Weight rows (the bulk of the bytes), all requested up front.
-  uint32_t wr[8][D];
+  // 2. This lane's pieces of its weight rows (and scale byte).
+  uint32_t wv[NL][PD];
+  uint32_t sb = 0;
   {
-    const uint32_t off = ((uint32_t(h) * K + k0) * kLatent + col) * ESZ; // < 2^22
+    const uint32_t off = ((uint32_t(h) * K + 32 * wave + r0) * kLatent + c0 + pcol) * ESZ; // < 2^22
     __builtin_assume(off < (1u << 22));
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      load_row<RB, NT>(static_cast<const uint8_t*>(a.w) + (off + uint32_t(r) * kLatent * ESZ), wr[r]);
-  }
-  uint32_t sc[8];
-  if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
-    const uint32_t off = (uint32_t(h) * K + k0) * kScalesPerRow + col / kMxBlock;
+    for (int v = 0; v < NL; ++v) {
+      const uint8_t* p = static_cast<const uint8_t*>(a.w) + (off + uint32_t(v) * RPL * kLatent * ESZ);
+      if constexpr (PD == 4) {
+        const u32x4_t x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
+                             : *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sc[r] = a.w_scales[off + uint32_t(r) * kScalesPerRow];
+        for (int d = 0; d < 4; ++d) wv[v][d] = x[d];
+      } else {
+        const u32x2_t x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p))
+                             : *reinterpret_cast<const u32x2_t*>(p);
+        wv[v][0] = x[0];
+        wv[v][1] = x[1];
+      }
+    }
+    if constexpr (WF == MLAQ_WEIGHT_MXFP8)
+      sb = a.w_scales[(uint32_t(h) * K + 32 * wave + r0) * kScalesPerRow + (c0 / kMxBlock)];
   }
 
   // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7. Rows past M read
@@ -136,24 +184,19 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
     const int mc = m < M ? m : 0;
     qa[t] = *at_byte<const u32x4_t>(a.q_nope, 2 * (__umul24(mc, a.q_sm) + __umul24(h, a.q_sh) + k0));
   }
-  __builtin_amdgcn_sched_barrier(0); // all loads are in flight before any wait
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 4. q_pe into columns 512..575 of its row (a bit copy, or the E4M3
-  //    conversion with the same per-tensor q_scale).
   float qs = 1.0f, rqs = 1.0f;
   if constexpr (OF == MLAQ_OUT_E4M3) {
     qs = *a.q_scale;
     rqs = 1.0f / qs;
   }
-  // Everything from here on, in two copies: x / q_scale by the one-FMA
-  // correction (the scales where it is exact), or by IEEE division (0, inf,
-  // NaN, subnormal or huge scales). The choice is uniform over the launch, so
-  // the usual copy runs as straight-line code.
   auto tail = [&](auto ieee_div) __attribute__((always_inline)) {
     auto quot = [&](float (&x)[4]) __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = decltype(ieee_div)::value ? x[c] / qs : div_rn(x[c], qs, rqs);
     };
+    // 4. q_pe into columns 512..575.
     if (has_pe) {
       const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
       if constexpr (OF == MLAQ_OUT_BF16) {
@@ -171,69 +214,70 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
         store_out<NT>(at_byte<u32x2_t>(a.out, o), v);
       }
     }
-    __builtin_amdgcn_sched_barrier(0); // the q_pe store leaves before the weight wait
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 5. Contraction over this wave's 32 k rows.
-    f32x4_t acc[MT][VEC];
+    // 5. The weight pieces as bf16 (exact decode for MXFP8) into this wave's
+    //    LDS tile, then the B fragments back through the transpose read.
+    uint8_t* wt = wtile + wave * 32 * TP;
+#pragma unroll
+    for (int v = 0; v < NL; ++v) {
+      uint32_t b[OD];
+      if constexpr (WF == MLAQ_WEIGHT_BF16) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) b[d] = wv[v][d];
+      } else {
+        const float sc = e8m0_scale_operand(sb);
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+          b[2 * d] = e4m3x2_scaled_bf16(wv[v][d], sc, false);
+          b[2 * d + 1] = e4m3x2_scaled_bf16(wv[v][d], sc, true);
+        }
+      }
+      uint8_t* dst = wt + (r0 + RPL * v) * TP + 2 * pcol;
+#pragma unroll
+      for (int q = 0; q < OD / 4; ++q)
+        *reinterpret_cast<u32x4_t*>(dst + 16 * q) = u32x4_t{b[4 * q], b[4 * q + 1], b[4 * q + 2], b[4 * q + 3]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    f32x4_t acc[MT][WC / 16];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if constexpr (WF == MLAQ_WEIGHT_BF16) {
+      for (int i = 0; i < WC / 16; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* src = wt + (8 * g + (j >> 2)) * TP + 8 * (j & 3);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t b;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          b[p] = __builtin_amdgcn_perm(wr[2 * p + 1][i >> 1], wr[2 * p][i >> 1], sel);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
-      }
-    } else {
-      // Exact decode, one scaled conversion per column pair and row: bf16 of
-      // E4M3 * 2^(S-127), laid out as the BF16 path's row dwords.
-      uint32_t wb[8][VEC / 2];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float s = e8m0_scale_operand(sc[r]);
-#pragma unroll
-        for (int e = 0; e < VEC; e += 2) wb[r][e >> 1] = e4m3x2_scaled_bf16(wr[r][e >> 2], s, (e >> 1) & 1);
-      }
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t b;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) b[p] = __builtin_amdgcn_perm(wb[2 * p + 1][i >> 1], wb[2 * p][i >> 1], sel);
+      for (int i = 0; i < WC / 16; ++i) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(src + 32 * i));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(src + 32 * i + 4 * TP));
+        const u32x4_t bf = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                            __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
 #pragma unroll
         for (int t = 0; t < MT; ++t)
           acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, b), acc[t][i], 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, bf), acc[t][i], 0, 0, 0);
       }
     }
 
-    // 5b. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
-    //    columns VEC*j + i.
+    // 6. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
+    //    column 16i + j.
     {
       float* pw = part + wave * MROWS * LDW;
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* dst = pw + (16 * t + 4 * g + r) * LDW + VEC * j;
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) dst[i] = acc[t][i][r];
-        }
+          for (int i = 0; i < WC / 16; ++i) pw[(16 * t + 4 * g + r) * LDW + 16 * i + j] = acc[t][i][r];
     }
     __syncthreads();
 
-    // 6. Epilogue: sum the k slices in a fixed order, round, convert and
+    // 7. Epilogue: sum the k slices in a fixed order, round, convert and
     //    store; each thread finishes 4 consecutive columns of one token.
-    constexpr int GPR = WCOLS / 4;
+    constexpr int GPR = WC / 4;
     for (int x = tid; x < M * GPR; x += THREADS) {
       const int m = x / GPR, cg = x - m * GPR;
       const int off = m * LDW + 4 * cg;
@@ -263,30 +307,22 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-// Columns per lane per k row: 2 for both weight formats and every M (32
-// columns and 16 workgroups per head; a 4-byte BF16 or 2-byte E4M3 row
-// segment per lane). Chosen by cold-cache timing of 2, 4 and 8 columns in
-// hipGraph loops; for MXFP8 at M <= 16, 4 columns (8 workgroups per head)
-// was ahead once, and is 3-5% behind 2 with the current kernel.
-template <int WF, int MT>
-constexpr int vec_of() {
-  return 2;
-}
-
 template <int WF, int OF, int MT, int NW, bool NT = false>
-const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, vec_of<WF, MT>(), NW, NT>);
+const void* kernel_ptr(int wc) {
+  if (wc == 16) return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 16>);
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 32>);
 }
 
 } // namespace
 
 const void* kernel_for(const Variant& v) {
+  if (v.cols != 16 && v.cols != 32) return nullptr;
 #define MLAQ_CASE(WF, OF, MT, K)                                                                 \
   if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT && v.nope == K) {      \
     if constexpr (WF == MLAQ_WEIGHT_BF16)                                                  \
-      return v.stream ? kernel_ptr<WF, OF, MT, K / 32, true>() : kernel_ptr<WF, OF, MT, K / 32>(); \
+      return v.stream ? kernel_ptr<WF, OF, MT, K / 32, true>(v.cols) : kernel_ptr<WF, OF, MT, K / 32>(v.cols); \
     else                                                                                   \
-      return v.stream ? nullptr : kernel_ptr<WF, OF, MT, K / 32>();                        \
+      return v.stream ? nullptr : kernel_ptr<WF, OF, MT, K / 32>(v.cols);                  \
   }
 #define MLAQ_CASES(K)                                \
   MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1, K)  \
@@ -305,11 +341,8 @@ const void* kernel_for(const Variant& v) {
 }
 
 void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
-  // The grid must use the column tile of the very kernel kernel_for() picks.
-  const bool bf = v.weight_format == MLAQ_WEIGHT_BF16, one = v.m_tiles == 1;
-  const int vec = bf ? (one ? vec_of<MLAQ_WEIGHT_BF16, 1>() : vec_of<MLAQ_WEIGHT_BF16, 2>())
-                     : (one ? vec_of<MLAQ_WEIGHT_MXFP8, 1>() : vec_of<MLAQ_WEIGHT_MXFP8, 2>());
-  *grid = dim3(unsigned(H * (kLatent / (16 * vec))), 1, 1);
+  // One workgroup per head and column tile of the kernel kernel_for() picks.
+  *grid = dim3(unsigned(H * (kLatent / v.cols)), 1, 1);
   *block = dim3(unsigned(64 * (v.nope / 32)), 1, 1);
 }
 

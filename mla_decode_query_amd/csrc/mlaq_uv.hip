@@ -45,7 +45,12 @@ constexpr int kUvScalesPerRow = kLatent / kMxBlock;
 // BF16 launches (bit-identical), 7.5% longer back-to-back calls on one warm
 // weight set; nontemporal output stores and MXFP8 rows gained nothing.
 template <int WF, int NMT, int CB, bool NT>
-__global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
+__global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_t* x, const void* w,
+                                                                   const uint8_t* w_scales, void* out, int M_,
+                                                                   int H_) {
+  // Scalar arguments (all preloaded into SGPRs with the wave, no
+  // kernel-argument load before the first weight request).
+  const UvArgs a{x, w, w_scales, out, M_, H_};
   constexpr int NVB = kValue / CB; // column blocks per head
   constexpr int MROWS = 16;        // tokens per workgroup
   constexpr int LDW = CB + 4;
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(UvArgs a) {
   const int j = lane & 15, g = lane >> 4;
   // Tile = (head, column block, token tile), the token tile fastest, so the
   // XCD-contiguous tile ranges keep both token tiles of a block together.
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int tile = tile_of_block(blockIdx.x, a.H * (NVB * NMT)); // the grid is H x NVB x NMT workgroups
   const int h = tile / (NVB * NMT), hr = tile - h * (NVB * NMT);
   const int vb = hr / NMT, mt = hr - (hr / NMT) * NMT;
   const int v = vb * CB + (j % CB); // this lane's value column
