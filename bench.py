@@ -22,7 +22,10 @@ Printed JSON line (stdout, one line):
               streaming hint): its algorithmic bytes per launch / its average
               launch duration, timed live with hipEvents over back-to-back
               cold launches, against the 8 TB/s HBM peak
-  per_call    warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
+  per_call_cold the metric per call on cold weights: H=16, M in {1,2,4,8,16,32},
+              BF16 and MXFP8 weights, BF16 and E4M3 output, us per call, GB/s
+              and roofline fraction, beside same-grid floors per weight format
+  per_call_warm warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
               MXFP8 weights (BF16 output), plus H=8 M=1 and H=11 M in
               {1,3,7,16,32} (BF16), with the staged torch baseline
   pages_shape the pages' own workload (K=192, H=8, M=1, BF16, 78 layers,
@@ -280,17 +283,15 @@ def decode_step_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     floors = floors_leg(torch, mq, layers, copies, stream, args)
     return {
-        "layers": layers, "ms": ms, "ms_default_hint": ms_default, "step_bytes": step_bytes, "dom_ms": dom_ms,
+        "layers": layers, "copies": copies, "stream": stream,
+        "ms": ms, "ms_default_hint": ms_default, "step_bytes": step_bytes, "dom_ms": dom_ms,
         "dom_ms_default_hint": dom[mq.MLAQ_CACHE_DEFAULT], "dom_bytes": dom_bytes,
         "staged_ms": staged_ms, "weight_bytes_per_copy": weight_bytes, "floors": floors, "nodes": nodes,
     }
 
 
-def floors_leg(torch, mq, layers, copies, stream, args):
-    """Per-node floors of the launch shape in the same graph loop as the
-    dominant kernel: an empty kernel (256 blocks x 256 threads) and a pure
-    read of each BF16 layer's 2 MiB weight slab (256 blocks, 8 KiB each, the
-    same cold rotation, no compute, no store)."""
+def diag_lib():
+    """The floor kernels (libmlaq_diag.so), or None when it is not built."""
     import ctypes
 
     path = ROOT / "mla_decode_query_amd" / "libmlaq_diag.so"
@@ -298,10 +299,20 @@ def floors_leg(torch, mq, layers, copies, stream, args):
         log("[bench] libmlaq_diag.so missing: floors skipped")
         return None
     diag = ctypes.CDLL(str(path))
-    diag.mlaqdiag_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    diag.mlaqdiag_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    P = ctypes.c_void_p
+    diag.mlaqdiag_empty.argtypes = [ctypes.c_int, P, P]
+    diag.mlaqdiag_read_grid.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, ctypes.c_int, P, P]
+    return diag
+
+
+def shape_floors(torch, diag, grid, weight_sets, stream, steps, warmup):
+    """Per-node floors of one launch shape, timed in the same cold graph loop
+    as the kernel they bound: the empty kernel on `grid` blocks, and a pure
+    read of each layer's weight bytes (payload, and scales when present) by
+    `grid` blocks, no compute, no store. weight_sets: one list of (w, scales
+    or None) per rotated copy, the layers of one graph."""
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
+    n = len(weight_sets[0])
 
     def capture(body):
         g = torch.cuda.CUDAGraph()
@@ -311,25 +322,95 @@ def floors_leg(torch, mq, layers, copies, stream, args):
         return g
 
     def empty_body(st):
-        for _ in bf:
-            assert diag.mlaqdiag_empty(256, sink.data_ptr(), st) == 0
+        for _ in range(n):
+            assert diag.mlaqdiag_empty(grid, sink.data_ptr(), st) == 0
 
-    def read_body_for(c):
+    def read_body_for(ws):
         def body(st):
-            for i in bf:
-                w = copies[c][i][0]
-                assert diag.mlaqdiag_stream_read(w.data_ptr(), w.numel() * w.element_size(), sink.data_ptr(), st) == 0
+            for w, s in ws:
+                nb = w.numel() * w.element_size()
+                assert diag.mlaqdiag_read_grid(w.data_ptr(), nb, None if s is None else s.data_ptr(),
+                                               0 if s is None else s.numel(), grid, sink.data_ptr(), st) == 0
         return body
 
     torch.cuda.synchronize()
     g_empty = [capture(empty_body)]
-    g_read = [capture(read_body_for(c)) for c in range(COPIES)]
+    g_read = [capture(read_body_for(ws)) for ws in weight_sets]
     torch.cuda.synchronize()
-    empty_us = time_graphs(torch, g_empty, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
-    read_us = time_graphs(torch, g_read, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
-    log(f"[bench] floors: empty kernel {empty_us:.3f} us/node, cold 2 MiB stream read {read_us:.3f} us/node")
-    return {"empty_kernel_us": round(empty_us, 4), "cold_read_2MiB_us": round(read_us, 4),
+    empty_us = time_graphs(torch, g_empty, steps, warmup, per_step_units=n) * 1e3
+    read_us = time_graphs(torch, g_read, steps, warmup, per_step_units=n) * 1e3
+    w, s = weight_sets[0][0]
+    nbytes = w.numel() * w.element_size() + (0 if s is None else s.numel())
+    return {"grid": grid, "empty_kernel_us": round(empty_us, 4), "cold_read_us": round(read_us, 4),
+            "read_bytes": nbytes}
+
+
+def floors_leg(torch, mq, layers, copies, stream, args):
+    """Per-node floors of the dominant kernel's launch shape (256 workgroups)
+    in the same graph loop: an empty kernel and a pure read of each BF16
+    layer's 2 MiB weight slab with the same cold rotation."""
+    diag = diag_lib()
+    if diag is None:
+        return None
+    bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
+    f = shape_floors(torch, diag, 256, [[copies[c][i] for i in bf] for c in range(COPIES)], stream, args.steps,
+                     args.warmup)
+    log(f"[bench] floors: empty kernel {f['empty_kernel_us']:.3f} us/node, cold 2 MiB read {f['cold_read_us']:.3f} us/node")
+    return {"empty_kernel_us": f["empty_kernel_us"], "cold_read_2MiB_us": f["cold_read_us"],
             "note": "per graph node, same grid as the dominant kernel; the read kernel moves the same weight bytes"}
+
+
+def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
+    """The metric per call, cold: for H = 16, each weight format, each output
+    dtype and M in {1,2,4,8,16,32}, the 32 layers of that format back to back
+    in one hipGraph per weight copy, the 6 copies replayed round-robin (every
+    layer's weights come from HBM), with the streaming cache hint; us per
+    call, algorithmic GB/s and the fraction of the 8 TB/s HBM peak, beside
+    the same-grid floors of each weight format (empty kernel; pure read of
+    the layer's weight bytes)."""
+    out_bf = {i: torch.empty((M_STEP, H, mq.ROW), dtype=torch.bfloat16, device="cuda") for i in range(len(layers))}
+    res = {"H": H, "layers_per_graph": None, "copies": COPIES, "cache_hint": "stream", "floors": {}}
+    diag = diag_lib()
+    for wf, wname in ((mq.MLAQ_WEIGHT_BF16, "bf16"), (mq.MLAQ_WEIGHT_MXFP8, "mxfp8")):
+        sel = [i for i, L in enumerate(layers) if L.wf == wf]
+        res["layers_per_graph"] = len(sel)
+        res[wname] = {}
+        for od, oname in ((mq.MLAQ_OUT_BF16, "bf16_out"), (mq.MLAQ_OUT_E4M3, "e4m3_out")):
+            res[wname][oname] = {}
+            for M in (1, 2, 4, 8, 16, 32):
+                def body(c, M=M, od=od):
+                    for i in sel:
+                        L = layers[i]
+                        w, s = copies[c][i]
+                        if od == mq.MLAQ_OUT_BF16:
+                            mq.mlaq_run_ex(L.q[:M], L.pe[:M], w, s, None, out_bf[i][:M], wf, od,
+                                           cache_hint=mq.MLAQ_CACHE_STREAM)
+                        else:
+                            mq.mlaq_run_ex(L.q[:M], L.pe[:M], w, s, L.qs, L.out[:M], wf, od,
+                                           cache_hint=mq.MLAQ_CACHE_STREAM)
+                graphs = []
+                for c in range(COPIES):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.stream(stream):
+                        with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                            body(c)
+                    graphs.append(g)
+                torch.cuda.synchronize()
+                us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=len(sel)) * 1e3
+                nbytes = wl.algorithmic_bytes(M, H, wf, od)
+                gbs = nbytes / (us * 1e-6) / 1e9
+                res[wname][oname][str(M)] = {"us": round(us, 4), "gbs": round(gbs, 1),
+                                             "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+                log(f"[bench] per-call cold {wname} W, {oname}, H={H} M={M}: {us:.3f} us, {gbs:.1f} GB/s "
+                    f"({gbs / HBM_PEAK_GBS:.4f} of peak)")
+                del graphs
+        if diag is not None:
+            f = shape_floors(torch, diag, H * 16, [[copies[c][i] for i in sel] for c in range(COPIES)], stream,
+                             args.steps, args.warmup)
+            res["floors"][wname] = f
+            log(f"[bench] per-call cold {wname} W floors ({f['grid']} workgroups): empty kernel "
+                f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us")
+    return res
 
 
 def per_call_leg(torch, mq, wl, reps=100, replays=20):
@@ -373,12 +454,14 @@ def per_call_leg(torch, mq, wl, reps=100, replays=20):
                         out[..., 512:].copy_(pe)
             us_staged = time_graphs(torch, [gs], replays, 3, per_step_units=reps) * 1e3
             nbytes = wl.algorithmic_bytes(M, H, wf, mq.MLAQ_OUT_BF16)
-            rows[str(M)] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            rows[str(M)] = {"us": round(us, 3), "gbs_cache_resident": round(nbytes / (us * 1e-6) / 1e9, 1),
                             "staged_us": round(us_staged, 3)}
-            log(f"[bench] per-call {name} H={H} M={M}: {us:.3f} us ({rows[str(M)]['gbs']} GB/s), "
-                f"staged {us_staged:.3f} us")
+            log(f"[bench] per-call warm {name} H={H} M={M}: {us:.3f} us "
+                f"({rows[str(M)]['gbs_cache_resident']} GB/s, cache-resident), staged {us_staged:.3f} us")
             del g, gs
         res[name] = rows
+    res["note"] = ("warm: one weight set called back to back, so the weights are served from the caches; "
+                   "the GB/s are not HBM figures (see per_call_cold)")
     return res
 
 
@@ -431,6 +514,13 @@ def pages_shape_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     f_us = time_graphs(torch, fg, args.steps, args.warmup, per_step_units=L) * 1e3
     s_us = time_graphs(torch, sg, args.steps, args.warmup, per_step_units=L) * 1e3
+    diag = diag_lib()
+    floors = None
+    if diag is not None:  # same grid as the fused kernel at this shape: H x 16 column tiles
+        floors = shape_floors(torch, diag, H8 * 16, [[(w, None) for w in wc[c]] for c in range(C)], stream,
+                              args.steps, args.warmup)
+        log(f"[bench] pages' shape floors ({floors['grid']} workgroups): empty kernel {floors['empty_kernel_us']:.3f} us, "
+            f"pure read of {floors['read_bytes']} B {floors['cold_read_us']:.3f} us")
 
     def fused_body():
         for d, w in zip(lay, wc[0]):
@@ -495,7 +585,7 @@ def pages_shape_leg(torch, mq, wl, args):
     return {"workload": "K=192 (GLM), H=8 (TP8), M=1, BF16 W and out, q_nope as a head-major [H,M,K] view, "
                         "78 layers per hipGraph, 4 rotated weight copies (cold)",
             "fused_us_per_layer": round(f_us, 4), "staged_us_per_layer": round(s_us, 4),
-            "graph_nodes_per_step": nodes,
+            "floors": floors, "graph_nodes_per_step": nodes,
             "pages_context_us_per_layer": {"fused": 2.880912, "staged": 4.047940,
                                            "hardware": "eight SM12x-class GPUs, averaged over ranks (not this GPU)"},
             "ab_ba_graph_replay": {"samples_per_shape": args.ab_samples, "shapes": ab}}
@@ -800,6 +890,8 @@ def main():
         print(json.dumps({args.only: leg(torch, mq, wl, args)}), flush=True)
         return
     step = decode_step_leg(torch, mq, wl, args)
+    per_call_cold = None if args.no_per_call else per_call_cold_leg(torch, mq, wl, args, step["layers"],
+                                                                     step["copies"], step["stream"])
     per_call = None if args.no_per_call else per_call_leg(torch, mq, wl)
     pages = None if args.no_pages_shape else pages_shape_leg(torch, mq, wl, args)
     uv = None if args.no_uv else uv_leg(torch, mq, wl, args)
@@ -841,7 +933,8 @@ def main():
         "staged": {"ms_per_step": round(step["staged_ms"], 5), "speedup": round(step["staged_ms"] / ms, 3),
                    "graph_nodes_per_step": step["nodes"]["staged"], "fused_graph_nodes_per_step": step["nodes"]["fused"]},
         "floors": step["floors"],
-        "per_call": per_call,
+        "per_call_cold": per_call_cold,
+        "per_call_warm": per_call,
         "pages_shape": pages,
         "uv_projection": uv,
         "attention": attn,

@@ -154,7 +154,9 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
  *   w, w_scales    contiguous [H, nope_dim, 512] and [H, nope_dim, 16]
  *
  * Requirements (else MLAQ_ERR_INVALID_ARG): strides >= 0, below 2^24 and
- * multiples of 8 elements; base pointers 16-byte aligned (q_scale 4-byte); the M*H output
+ * multiples of 8 elements, the head strides of q_nope and q_pe (q_stride_h,
+ * pe_stride_h) below 2^16 (a head-major [H,M,K] view needs M*K <= 6144);
+ * base pointers 16-byte aligned (q_scale 4-byte); the M*H output
  * rows pairwise disjoint (one outer stride >= 576 and the other >= the first
  * times its extent); the output's address span disjoint from every input's.
  * nope_dim must be 128 or 192 (else MLAQ_ERR_UNSUPPORTED). Everything else is

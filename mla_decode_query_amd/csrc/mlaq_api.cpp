@@ -222,6 +222,8 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
   if (!stride_ok(a.q_stride_m) || !stride_ok(a.q_stride_h) || !stride_ok(a.pe_stride_m) ||
       !stride_ok(a.pe_stride_h) || !stride_ok(a.out_stride_m) || !stride_ok(a.out_stride_h))
     return fail(MLAQ_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements below 2^24");
+  if (a.q_stride_h >= mlaq::kMaxHeadStride || a.pe_stride_h >= mlaq::kMaxHeadStride)
+    return fail(MLAQ_ERR_INVALID_ARG, "head strides of q_nope and q_pe must be below 2^16 elements");
   if (!rows_disjoint(M, H, a.out_stride_m, a.out_stride_h))
     return fail(MLAQ_ERR_INVALID_ARG, "out strides (%lld, %lld) make output rows overlap",
                 (long long)a.out_stride_m, (long long)a.out_stride_h);
@@ -254,8 +256,11 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream) {
                      static_cast<const uint8_t*>(a.w_scales), a.q_scale, a.out,
                      uint32_t(a.q_stride_m), uint32_t(a.q_stride_h), uint32_t(a.pe_stride_m),
                      uint32_t(a.pe_stride_h), uint32_t(a.out_stride_m), uint32_t(a.out_stride_h), M, H};
-  void* kargs[] = {&ka.q_pe, &ka.w, &ka.q_nope, &ka.w_scales, &ka.pe_sm, &ka.pe_sh, &ka.q_sm,
-                   &ka.q_sh, &ka.M, &ka.H, &ka.out, &ka.q_scale, &ka.out_sm, &ka.out_sh};
+  // The kernel's argument order (the first 14 dwords are preloaded): head
+  // strides and (M, H) travel packed as two 16-bit halves each.
+  uint32_t head_strides = ka.q_sh | (ka.pe_sh << 16), m_h = uint32_t(M) | (uint32_t(H) << 16);
+  void* kargs[] = {&ka.q_pe, &ka.w, &ka.q_nope, &ka.w_scales, &ka.q_scale, &ka.pe_sm, &ka.q_sm,
+                   &head_strides, &m_h, &ka.out, &ka.out_sm, &ka.out_sh};
   e = hipLaunchKernel(fn, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
   return MLAQ_OK;

@@ -1,9 +1,10 @@
 // mlaq_diag.hip -- measurement floors for the benchmark (libmlaq_diag.so).
-// Not part of the fused path. Two kernels give the cost of the launch shape
-// itself in a hipGraph: one that does nothing, and one that streams the same
-// bytes as the fused kernel's weight read (each 256-thread block reads 8 KiB,
-// 16 bytes per lane per load) and writes nothing, so their per-node times are
-// the floors the fused kernel's time is compared against.
+// Not part of the fused path. The kernels give the cost of a launch shape
+// itself in a hipGraph: one that does nothing, and one that streams given
+// byte ranges in as many blocks as the measured kernel has workgroups (each
+// block reads its contiguous share, 16 bytes per lane per load, every load
+// issued before any wait) and writes nothing. Their per-node times are the
+// floors a fused kernel of that grid is compared against.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -16,12 +17,25 @@ __global__ __launch_bounds__(256) void empty_kernel(uint32_t* sink) {
   if (threadIdx.x == 0xffffu) sink[0] = 1u; // never true: keeps the kernel non-empty for the compiler
 }
 
-// Block b reads bytes [8 KiB * b, 8 KiB * (b + 1)) of p.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, uint32_t* sink) {
-  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p + size_t(blockIdx.x) * 8192) + threadIdx.x;
-  const u32x4_t a = q[0];
-  const u32x4_t b = q[256];
-  const uint32_t x = a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+// Block b reads bytes [per * b, per * (b + 1)) of p (per = NL * 4096: NL
+// loads of 16 bytes per lane) and, when p2 is not null, bytes
+// [per2 * b, per2 * (b + 1)) of p2 (per2 <= 4096, a multiple of 16; lanes
+// past it re-read the block's first 16 bytes, which adds no HBM traffic).
+template <int NL>
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, const uint8_t* p2, uint32_t per2,
+                                                          uint32_t* sink) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p + size_t(blockIdx.x) * (NL * 4096)) + threadIdx.x;
+  u32x4_t v[NL + 1];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) v[i] = q[256 * i];
+  v[NL] = u32x4_t{0u, 0u, 0u, 0u};
+  if (p2) {
+    const uint32_t o = 16 * threadIdx.x < per2 ? 16 * threadIdx.x : 0;
+    v[NL] = *reinterpret_cast<const u32x4_t*>(p2 + size_t(blockIdx.x) * per2 + o);
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i <= NL; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
   if (x == 0x9e3779b9u && threadIdx.x == 0) sink[0] = x; // data-dependent, practically never taken
 }
 
@@ -38,16 +52,38 @@ int mlaqdiag_empty(int grid, void* sink, void* stream) {
                              static_cast<hipStream_t>(stream)));
 }
 
-// Enqueue a read of `bytes` bytes at `p` (16-byte aligned, bytes a positive
-// multiple of 8192): bytes / 8192 blocks of 256 threads. Returns 0 or a
-// hipError_t value.
-int mlaqdiag_stream_read(const void* p, size_t bytes, void* sink, void* stream) {
-  if (!p || !sink || bytes == 0 || bytes % 8192 != 0 || (reinterpret_cast<uintptr_t>(p) & 15) != 0)
+// Enqueue a read of `bytes` bytes at `p` in `grid` blocks of 256 threads
+// (bytes / grid must be 4096, 8192, 12288 or 16384), plus `bytes2` bytes at
+// `p2` spread over the same blocks (p2 may be null with bytes2 = 0;
+// otherwise bytes2 / grid must be a multiple of 16 of at most 4096). Both
+// pointers 16-byte aligned. Returns 0 or a hipError_t value.
+int mlaqdiag_read_grid(const void* p, size_t bytes, const void* p2, size_t bytes2, int grid, void* sink,
+                       void* stream) {
+  if (!p || !sink || grid < 1 || bytes % size_t(grid) != 0 || (reinterpret_cast<uintptr_t>(p) & 15) != 0)
     return int(hipErrorInvalidValue);
+  if (p2 ? (bytes2 % size_t(grid) != 0 || (bytes2 / grid) % 16 != 0 || bytes2 / grid > 4096 ||
+            bytes2 / grid == 0 || (reinterpret_cast<uintptr_t>(p2) & 15) != 0)
+         : bytes2 != 0)
+    return int(hipErrorInvalidValue);
+  const size_t per = bytes / size_t(grid);
+  const void* fn = per == 4096    ? reinterpret_cast<const void*>(&stream_read_kernel<1>)
+                   : per == 8192  ? reinterpret_cast<const void*>(&stream_read_kernel<2>)
+                   : per == 12288 ? reinterpret_cast<const void*>(&stream_read_kernel<3>)
+                   : per == 16384 ? reinterpret_cast<const void*>(&stream_read_kernel<4>)
+                                  : nullptr;
+  if (!fn) return int(hipErrorInvalidValue);
   const uint8_t* pp = static_cast<const uint8_t*>(p);
-  void* args[] = {&pp, &sink};
-  return int(hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_kernel), dim3(unsigned(bytes / 8192)),
-                             dim3(256), args, 0, static_cast<hipStream_t>(stream)));
+  const uint8_t* pp2 = static_cast<const uint8_t*>(p2);
+  uint32_t per2 = uint32_t(p2 ? bytes2 / size_t(grid) : 0);
+  void* args[] = {&pp, &pp2, &per2, &sink};
+  return int(hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
+}
+
+// The 2 MiB-per-layer form used since the first benchmark: `bytes` (a
+// positive multiple of 8192) in bytes / 8192 blocks.
+int mlaqdiag_stream_read(const void* p, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0 || bytes % 8192 != 0) return int(hipErrorInvalidValue);
+  return mlaqdiag_read_grid(p, bytes, nullptr, 0, int(bytes / 8192), sink, stream);
 }
 
 } // extern "C"

@@ -18,6 +18,7 @@ constexpr int kMxBlock = 32; // E8M0 scale group along n
 constexpr int kValue = 128;  // V: value width of the UV projection
 constexpr int kMaxM = 32;
 constexpr int64_t kMaxStride = int64_t(1) << 24; // elements; keeps kernel offsets 32-bit
+constexpr int64_t kMaxHeadStride = int64_t(1) << 16; // q_nope / q_pe head strides travel as 16-bit halves
 
 // Kernel arguments, passed by value (one kernarg segment). Strides are in
 // elements (below 2^24, so offsets stay 32-bit and multiplies 24-bit); the

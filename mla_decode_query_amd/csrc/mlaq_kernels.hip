@@ -36,8 +36,8 @@
 // The waves' fp32 partial tiles are summed through LDS in a fixed order
 // (wave 0 + 1 + 2 + ...), so results are deterministic. The epilogue rounds to
 // bf16 (and for E4M3 output divides by q_scale and encodes), and the same
-// workgroups copy q_pe into columns 512..575 of the row, storing it before
-// they wait for their weights.
+// workgroups copy q_pe into columns 512..575 of the row (a BF16 copy leaves
+// before the weights arrive, an E4M3 one right after).
 //
 // Cache policy. A decode step reads each layer's weights once, cold in HBM;
 // the MLAQ_CACHE_STREAM kernels (template flag NT, BF16 weights only) load
@@ -98,14 +98,17 @@ struct Flag {
 
 template <int WF, int OF, int MT, int NW, bool NT, int WC>
 __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
-    const uint16_t* q_pe, const void* w, const uint16_t* q_nope, const uint8_t* w_scales, uint32_t pe_sm,
-    uint32_t pe_sh, uint32_t q_sm, uint32_t q_sh, int M_, int H_, void* out, const float* q_scale, uint32_t out_sm,
-    uint32_t out_sh) {
-  // Scalar arguments, ordered so that everything the first loads need lies
-  // in the first 16 dwords of the kernel-argument segment: with kernel
-  // argument preloading those arrive in SGPRs with the wave, and no wave waits
-  // for a kernel-argument load before it can request its data.
-  const FusedArgs a{q_nope, q_pe, w, w_scales, q_scale, out, q_sm, q_sh, pe_sm, pe_sh, out_sm, out_sh, M_, H_};
+    const uint16_t* q_pe, const void* w, const uint16_t* q_nope, const uint8_t* w_scales, const float* q_scale,
+    uint32_t pe_sm, uint32_t q_sm, uint32_t head_strides, uint32_t m_h, void* out, uint32_t out_sm, uint32_t out_sh) {
+  // Scalar arguments, ordered so that everything the first requests need
+  // (the input pointers, q_scale's among them, and the input strides, M and
+  // H) lies in the 14 dwords of the kernel-argument segment that are
+  // preloaded into SGPRs with the wave: no wave waits for a kernel-argument
+  // load before it requests its data, and q_scale is one memory round trip
+  // away, not two. head_strides packs the head strides of q_nope (low 16
+  // bits) and q_pe (high), m_h packs M (low 16 bits) and H (high).
+  const FusedArgs a{q_nope, q_pe, w, w_scales, q_scale, out, q_sm, head_strides & 0xffffu, pe_sm,
+                    head_strides >> 16, out_sm, out_sh, int(m_h & 0xffffu), int(m_h >> 16)};
   constexpr int K = 32 * NW;
   constexpr int THREADS = 64 * NW;
   constexpr int NCT = kLatent / WC;
@@ -196,11 +199,19 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = decltype(ieee_div)::value ? x[c] / qs : div_rn(x[c], qs, rqs);
     };
-    // 4. q_pe into columns 512..575.
+    // 4. q_pe into columns 512..575. Loads and stores share one counter of
+    //    outstanding memory operations, so a store issued before the last
+    //    load has arrived must be acknowledged before that load can be
+    //    waited for. The BF16 bit copy leaves as soon as q_pe arrives (its
+    //    acknowledgement returns while the weights are still in flight); the
+    //    E4M3 conversion also needs q_scale, so its store is held back until
+    //    the weights have arrived (step 6), which measured 6-8% shorter MXFP8
+    //    launches and no change for BF16 weights.
+    const uint32_t pe_o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
+    u32x2_t pe_e4 = {0u, 0u};
     if (has_pe) {
-      const uint32_t o = __umul24(pe_m, a.out_sm) + __umul24(h, a.out_sh) + kLatent + 8 * pe_c;
       if constexpr (OF == MLAQ_OUT_BF16) {
-        store_out<NT>(at_byte<u32x4_t>(a.out, 2 * o), pe_v);
+        store_out<NT>(at_byte<u32x4_t>(a.out, 2 * pe_o), pe_v);
       } else {
         float x[2][4];
 #pragma unroll
@@ -208,10 +219,8 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
           x[c >> 2][c & 3] = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
         quot(x[0]);
         quot(x[1]);
-        u32x2_t v;
-        v[0] = e4m3x4_satfinite(x[0][0], x[0][1], x[0][2], x[0][3]);
-        v[1] = e4m3x4_satfinite(x[1][0], x[1][1], x[1][2], x[1][3]);
-        store_out<NT>(at_byte<u32x2_t>(a.out, o), v);
+        pe_e4[0] = e4m3x4_satfinite(x[0][0], x[0][1], x[0][2], x[0][3]);
+        pe_e4[1] = e4m3x4_satfinite(x[1][0], x[1][1], x[1][2], x[1][3]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -262,6 +271,9 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
       }
     }
 
+    if constexpr (OF == MLAQ_OUT_E4M3) {
+      if (has_pe) store_out<NT>(at_byte<u32x2_t>(a.out, pe_o), pe_e4);
+    }
     // 6. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
     //    column 16i + j.
     {

@@ -188,6 +188,8 @@ def run_ex(lib, **kw):
     (dict(pe_stride_h=4), INV, "strides"),
     (dict(out_stride_h=572), INV, "strides"),
     (dict(out_stride_h=1 << 24), INV, "strides"),
+    (dict(q_stride_h=1 << 16), INV, "head strides"),   # head strides travel as 16-bit halves
+    (dict(pe_stride_h=1 << 16), INV, "head strides"),
     (dict(out_stride_h=568), INV, "overlap"),          # rows of 576 elements would overlap
     (dict(out_stride_m=576 * 8), INV, "overlap"),      # m-major but tokens collide with heads
     (dict(out_stride_m=0, out_stride_h=576), INV, "overlap"),
