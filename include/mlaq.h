@@ -245,14 +245,15 @@ int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, voi
  *
  * The tokens are cut into num_splits ranges of ceil(T/S) rounded up to 64
  * tokens; each range stores its normalized output (MLAQ_PARTIAL_BF16, the
- * default, or MLAQ_PARTIAL_FP32, which avoids the intermediate rounding and
- * doubles the partial bytes) and its lse in fp32 in the caller's workspace,
+ * default, or MLAQ_PARTIAL_FP32, which avoids the intermediate roundings --
+ * the softmax weights enter the value product with 16 significant bits
+ * instead of 8 -- and doubles the partial bytes) and its lse in fp32 in the caller's workspace,
  * and a merge kernel forms the BF16 output. With num_splits = 1 the single
  * range is written straight to `out` (identical result, no merge launch).
  * T_m = 0 gives out = 0 and lse = -inf.
  *
  *   q             bf16 [M,H,576] at q + m*q_stride_m + h*q_stride_h (elements,
- *                 multiples of 8), rows contiguous, 16-byte aligned
+ *                 multiples of 8 below 2^31), rows contiguous, 16-byte aligned
  *   kv_cache      bf16 [num_pages, page_size, 576], contiguous, 16-byte aligned
  *   block_table   int32 [M, block_table_stride], 4-byte aligned
  *   seq_lens      int32 [M], 4-byte aligned

@@ -489,8 +489,9 @@ int attn_run(const mlaq_attn_args* args, bool use_scratch, void* stream) {
     return fail(MLAQ_ERR_UNSUPPORTED, "block_table_stride * page_size exceeds 2^30 tokens");
   if (!(a.softmax_scale == a.softmax_scale) || a.softmax_scale > 3.4e38f || a.softmax_scale < -3.4e38f)
     return fail(MLAQ_ERR_INVALID_ARG, "softmax_scale must be finite");
-  if (a.q_stride_m < 0 || a.q_stride_h < 0 || a.q_stride_m % 8 || a.q_stride_h % 8)
-    return fail(MLAQ_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements");
+  if (a.q_stride_m < 0 || a.q_stride_h < 0 || a.q_stride_m % 8 || a.q_stride_h % 8 ||
+      a.q_stride_m >= (int64_t(1) << 31) || a.q_stride_h >= (int64_t(1) << 31))
+    return fail(MLAQ_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements below 2^31");
   if (!aligned(a.q, 16) || !aligned(a.kv_cache, 16) || !aligned(a.out, 16))
     return fail(MLAQ_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
   if (!aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.lse, 4))
@@ -561,7 +562,12 @@ int attn_run(const mlaq_attn_args* args, bool use_scratch, void* stream) {
   ka.S = a.num_splits;
   dim3 split_grid, merge_grid, block;
   mlaq::attn_launch_shapes(a.M, a.H, a.num_splits, &split_grid, &merge_grid, &block);
-  void* kargs[] = {&ka};
+  // The kernels' scalar arguments (S, H and M packed into one word).
+  uint32_t q_sm32 = uint32_t(ka.q_sm), q_sh32 = uint32_t(ka.q_sh);
+  uint32_t shm = uint32_t(ka.S) | (uint32_t(ka.H) << 9) | (uint32_t(ka.M) << 14);
+  void* split_args[] = {&ka.seq_lens, &ka.bt, &ka.kv, &ka.q, &q_sm32, &q_sh32, &shm, &ka.P, &ka.bt_stride,
+                        &ka.num_pages, &ka.part, &ka.part_lse, &ka.out, &ka.lse, &ka.scale_log2};
+  void* merge_args[] = {&ka.part_lse, &ka.part, &ka.out, &ka.lse, &shm};
   const hipStream_t st_ = static_cast<hipStream_t>(stream);
   const bool direct = a.num_splits == 1;
   int parts = 1, per_thread = 1;
@@ -571,12 +577,12 @@ int attn_run(const mlaq_attn_args* args, bool use_scratch, void* stream) {
   const void* split_fn = mlaq::attn_split_kernel_for(a.partial_dtype, direct);
   const void* merge_fn = direct ? nullptr : mlaq::attn_merge_kernel_for(a.partial_dtype, parts, per_thread);
   if (!split_fn || (!direct && !merge_fn)) return fail(MLAQ_ERR_UNSUPPORTED, "no attention kernel for this plan");
-  e = hipLaunchKernel(split_fn, split_grid, block, kargs, 0, st_);
+  e = hipLaunchKernel(split_fn, split_grid, block, split_args, 0, st_);
   if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "split kernel launch: %s", hipGetErrorString(e));
   if (!direct) {
     // The split kernel of a multi-split call writes only the workspace, so a
     // failed merge launch still leaves out and lse untouched.
-    e = hipLaunchKernel(merge_fn, merge_grid, block, kargs, 0, st_);
+    e = hipLaunchKernel(merge_fn, merge_grid, block, merge_args, 0, st_);
     if (e != hipSuccess)
       return fail(MLAQ_ERR_DEVICE, "merge kernel launch (the split kernel, which writes only the workspace, is "
                                    "enqueued): %s", hipGetErrorString(e));

@@ -36,7 +36,9 @@
 //  - online softmax in the log2 domain: the row max over the tile is reduced
 //    across the 16 lanes of a row with DPP and across the 4 waves through
 //    LDS; the running sums stay per lane until the end;
-//  - P (bf16) goes to LDS; wave w multiplies it by the value columns
+//  - P (bf16; for FP32 partials also its bf16 remainder, so that P enters
+//    the value product with 16 significant bits) goes to LDS; wave w
+//    multiplies it by the value columns
 //    [128w, 128w+128): 2 k-blocks of 32 tokens x 8 column tiles. The value
 //    B fragments come from the row-major tile through the gfx950 LDS
 //    transpose read (two 8-byte reads per fragment), with no gathers.
@@ -145,22 +147,56 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int m) {
 // neighbouring column parts, whose 64-byte partial segments share 128-byte
 // lines, fetch each line once (the 64k merge's fetch halves). Measured 1.2-1.4%
 // shorter calls with bit-identical results.
-__device__ __forceinline__ int xcd_local_block() {
-  const int n = gridDim.x;
+__device__ __forceinline__ int xcd_local_block(int n) { // n: the grid's block count
   return (n & 7) == 0 ? dev::tile_of_block(blockIdx.x, n) : int(blockIdx.x);
 }
 
+// (S, H, M) travel packed in one kernel argument: S in bits 0-8, H in 9-13,
+// M in 14-30 (S <= 256, H <= 16, M <= 65536).
+__device__ __forceinline__ void unpack_shm(uint32_t shm, int* S, int* H, int* M) {
+  *S = int(shm & 0x1ffu);
+  *H = int((shm >> 9) & 0x1fu);
+  *M = int(shm >> 14);
+}
+
+// Scalar arguments: the first 14 dwords (everything the start-up chain of
+// length -> block table -> cache row needs, and the query rows) are preloaded
+// into SGPRs with the wave, so no wave waits for a kernel-argument load first.
 template <int PD>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
+    const int32_t* seq_lens_, const int32_t* bt_, const uint16_t* kv_, const uint16_t* q_, uint32_t q_sm_,
+    uint32_t q_sh_, uint32_t shm_, int P_, int bt_stride_, int num_pages_, void* part_, float* part_lse_,
+    uint16_t* out_, float* lse_, float scale_log2_) {
+  AttnArgs a{};
+  a.q = q_;
+  a.kv = kv_;
+  a.bt = bt_;
+  a.seq_lens = seq_lens_;
+  a.part = part_;
+  a.part_lse = part_lse_;
+  a.out = out_;
+  a.lse = lse_;
+  a.q_sm = q_sm_;
+  a.q_sh = q_sh_;
+  a.scale_log2 = scale_log2_;
+  unpack_shm(shm_, &a.S, &a.H, &a.M);
+  a.P = P_;
+  a.num_pages = num_pages_;
+  a.bt_stride = bt_stride_;
+  // FP32 partials keep P to 16 significant bits: P = hi + lo, two bf16
+  // tiles and two value products, so the partial is not limited by a bf16
+  // rounding of the softmax weights. BF16 partials (and the one-split form,
+  // whose output is bf16) use P rounded to bf16 once.
+  constexpr bool kSplitP = PD == kPartialFp32;
   __shared__ __attribute__((aligned(16))) uint8_t kvt[kTileBytes]; // the current tile, row = token
-  __shared__ __attribute__((aligned(16))) uint16_t pt[16 * kPPitch];  // P tile (bf16), row = head
+  __shared__ __attribute__((aligned(16))) uint16_t pt[(kSplitP ? 2 : 1) * 16 * kPPitch]; // P (hi, lo), row = head
   __shared__ __attribute__((aligned(16))) float red[4][16];            // per-wave row max / sum
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   const int S = a.S;
-  const int bx = xcd_local_block();
+  const int bx = xcd_local_block(a.M * a.S);
   const int m = bx / S, s = bx - (bx / S) * S;
   const int H = a.H;
   const int T = clamp_len(a, m);
@@ -299,13 +335,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       l_run[r] = l_run[r] * alpha[r] + p;
       sc[r] = p;
     }
-    // 4. P (bf16) into LDS in slot order; rescale the output accumulators.
+    // 4. P (bf16, and for FP32 partials its bf16 remainder p - hi, exact in
+    //    fp32) into LDS in slot order; rescale the output accumulators.
     {
       const uint32_t p01 = bf16x2_rne(sc[0], sc[1]), p23 = bf16x2_rne(sc[2], sc[3]);
       pt[(4 * g + 0) * kPPitch + pslot] = uint16_t(p01);
       pt[(4 * g + 1) * kPPitch + pslot] = uint16_t(p01 >> 16);
       pt[(4 * g + 2) * kPPitch + pslot] = uint16_t(p23);
       pt[(4 * g + 3) * kPPitch + pslot] = uint16_t(p23 >> 16);
+      if constexpr (kSplitP) {
+        const uint32_t l01 = bf16x2_rne(sc[0] - __uint_as_float(p01 << 16), sc[1] - __uint_as_float(p01 & 0xffff0000u));
+        const uint32_t l23 = bf16x2_rne(sc[2] - __uint_as_float(p23 << 16), sc[3] - __uint_as_float(p23 & 0xffff0000u));
+        uint16_t* plo = pt + 16 * kPPitch;
+        plo[(4 * g + 0) * kPPitch + pslot] = uint16_t(l01);
+        plo[(4 * g + 1) * kPPitch + pslot] = uint16_t(l01 >> 16);
+        plo[(4 * g + 2) * kPPitch + pslot] = uint16_t(l23);
+        plo[(4 * g + 3) * kPPitch + pslot] = uint16_t(l23 >> 16);
+      }
     }
     // (skipped when no row maximum of this wave's rows moved: alpha is then 1)
     if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
@@ -327,6 +373,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pt + j * kPPitch + 32 * kb2 + 8 * g);
+        u32x4_t pl = {0u, 0u, 0u, 0u};
+        if constexpr (kSplitP) pl = *reinterpret_cast<const u32x4_t*>(pt + (16 + j) * kPPitch + 32 * kb2 + 8 * g);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const uint8_t* vp = vsrc + 32 * kb2 * kVPitch + 32 * ct;
@@ -336,6 +384,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
                               __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
                                                             __builtin_bit_cast(bf16x8_t, vb), acc[ct], 0, 0, 0);
+          if constexpr (kSplitP)
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pl),
+                                                              __builtin_bit_cast(bf16x8_t, vb), acc[ct], 0, 0, 0);
         }
       }
     }
@@ -442,7 +493,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // are then added in a fixed order: four per thread into QN slices, then the
 // QN slices (deterministic, no atomics).
 template <int PD, int QN, int R>
-__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float* part_lse_, const void* part_,
+                                                                  uint16_t* out_, float* lse_, uint32_t shm_) {
+  // Scalar arguments, all preloaded into SGPRs with the wave.
+  AttnArgs a{};
+  a.part_lse = const_cast<float*>(part_lse_);
+  a.part = const_cast<void*>(part_);
+  a.out = out_;
+  a.lse = lse_;
+  unpack_shm(shm_, &a.S, &a.H, &a.M);
   constexpr int kCols = kLatent / QN;         // columns per workgroup
   constexpr int CG = kCols / 8;               // column groups (8 columns each)
   constexpr int RG = kAttnThreads / CG;       // range groups (4 QN)
@@ -457,7 +516,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float part_sum[RG][kCols];
   __shared__ __attribute__((aligned(8))) float slice_sum[KS][kCols];
   const int H = a.H, S = a.S;
-  const int bx = xcd_local_block();
+  const int bx = xcd_local_block(a.M * a.H * QN);
   const int mh = bx / QN, part = bx - (bx / QN) * QN;
   const int m = mh / H, h = mh - (mh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

@@ -197,7 +197,10 @@ def assert_attn_parity(gpu, gpu_lse, ref, inp, S, pd, what, ws=None):
         upart = np.max(np.where(ok, ustore, 0.0), axis=1)
         lse_mag = np.maximum(lse_mag, np.max(np.abs(np.where(np.isfinite(ref["plse"]), ref["plse"], 0.0)), axis=1))
     dlse = 2.0 ** -20 * (1 + lse_mag) + 2 * gT + eps  # [M,H]
-    bound = (ulp_bf16(o) + upart + (2.0 ** -8 + 4 * eps[..., None] + 4 * gT[..., None]) * ref["vabs"]
+    # The softmax weights enter the value product rounded to bf16 (2^-9,
+    # doubled), or with FP32 partials as a bf16 pair hi + lo (16 bits).
+    pterm = 2.0 ** -16 if (pd == FP32P and S > 1) else 2.0 ** -8
+    bound = (ulp_bf16(o) + upart + (pterm + 4 * eps[..., None] + 4 * gT[..., None]) * ref["vabs"]
              + 4 * dlse[..., None] * vmax + 2.0 ** -20 * np.max(np.abs(o)))
     bad = ~(np.abs(got - o) <= bound)
     assert not bad.any(), (f"{what}: {int(bad.sum())} outputs outside the bound, first {np.argwhere(bad)[0]}: "
@@ -215,7 +218,7 @@ def assert_attn_parity(gpu, gpu_lse, ref, inp, S, pd, what, ws=None):
         ok = np.isfinite(ref["plse"])
         assert np.array_equal(np.isneginf(plse), ~ok), f"{what}: empty ranges must store lse = -inf"
         ustore = ulp_bf16(ref["part"]) if pd == BF16P else ulp_f32(ref["part"])
-        pb = ustore + (2.0 ** -8 + 4 * eps[:, None, :, None] + 4 * gT[:, :, None, None]) * ref["pvabs"]
+        pb = ustore + (pterm + 4 * eps[:, None, :, None] + 4 * gT[:, :, None, None]) * ref["pvabs"]
         pbad = ok[..., None] & ~(np.abs(part - ref["part"]) <= pb)
         assert not pbad.any(), f"{what}: {int(pbad.sum())} partials outside the bound, first {np.argwhere(pbad)[0]}"
         lb = 2.0 ** -20 * (1 + np.abs(np.where(ok, ref["plse"], 0))) + 2 * gT[:, :, None] + eps[:, None, :]

@@ -386,6 +386,7 @@ def attn_run(lib, **kw):
     (dict(softmax_scale=float("inf")), INV, "finite"),
     (dict(q_stride_h=100), INV, "multiples of 8"),
     (dict(q_stride_m=-8), INV, "multiples of 8"),
+    (dict(q_stride_m=1 << 31), INV, "below 2^31"),  # strides travel as 32-bit kernel arguments
     (dict(q=A + 8), INV, "16-byte aligned"),
     (dict(kv_cache=64 * A + 4), INV, "16-byte aligned"),
     (dict(out=4 * A + 2), INV, "16-byte aligned"),

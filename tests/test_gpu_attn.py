@@ -101,9 +101,9 @@ def test_attn_heads_and_page_sizes(H, P, lens):
 def test_attn_decode_batch_full_size():
     """The measured workload: 32 sequences of 4096 cached tokens, 16 heads,
     the library's split count; both partial dtypes. Against the exact split
-    partials, FP32 storage errs clearly less than BF16 storage (over 4 M
-    values; the remaining FP32 error is the bf16 P operand of the value
-    product, about 2^-10 relative)."""
+    partials (over 4 M values), FP32 partials err at least 4x less than BF16
+    ones: they keep the softmax weights to 16 bits in the value product and
+    store fp32, where BF16 partials round both to bf16."""
     H, M, T = 16, 32, 4096
     inp = cached_inputs(8200, H, [T] * M)
     d = Dev(inp)
@@ -116,7 +116,8 @@ def test_attn_decode_batch_full_size():
         assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"full size pd={pd}", ws)
         part, _ = read_partials(ws, M, H, S, pd)
         perr[pd] = np.linalg.norm(part - exact["part"]) / np.linalg.norm(exact["part"])
-    assert perr[FP32P] < 0.75 * perr[BF16P], f"partial errors fp32 {perr[FP32P]} vs bf16 {perr[BF16P]}"
+    assert perr[FP32P] < 0.25 * perr[BF16P], f"partial errors fp32 {perr[FP32P]} vs bf16 {perr[BF16P]}"
+    print(f"relative L2 error of the partials against exact ones: fp32 {perr[FP32P]:.3e}, bf16 {perr[BF16P]:.3e}")
 
 
 def test_attn_long_context():
