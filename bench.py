@@ -516,8 +516,8 @@ def pages_shape_leg(torch, mq, wl, args):
     s_us = time_graphs(torch, sg, args.steps, args.warmup, per_step_units=L) * 1e3
     diag = diag_lib()
     floors = None
-    if diag is not None:  # same grid as the fused kernel at this shape: H x 16 column tiles
-        floors = shape_floors(torch, diag, H8 * 16, [[(w, None) for w in wc[c]] for c in range(C)], stream,
+    if diag is not None:  # same grid as the fused kernel at this shape: 16-column tiles at H = 8, M <= 16
+        floors = shape_floors(torch, diag, H8 * 32, [[(w, None) for w in wc[c]] for c in range(C)], stream,
                               args.steps, args.warmup)
         log(f"[bench] pages' shape floors ({floors['grid']} workgroups): empty kernel {floors['empty_kernel_us']:.3f} us, "
             f"pure read of {floors['read_bytes']} B {floors['cold_read_us']:.3f} us")

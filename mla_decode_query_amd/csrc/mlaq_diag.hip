@@ -17,17 +17,21 @@ __global__ __launch_bounds__(256) void empty_kernel(uint32_t* sink) {
   if (threadIdx.x == 0xffffu) sink[0] = 1u; // never true: keeps the kernel non-empty for the compiler
 }
 
-// Block b reads bytes [per * b, per * (b + 1)) of p (per = NL * 4096: NL
-// loads of 16 bytes per lane) and, when p2 is not null, bytes
-// [per2 * b, per2 * (b + 1)) of p2 (per2 <= 4096, a multiple of 16; lanes
-// past it re-read the block's first 16 bytes, which adds no HBM traffic).
+// Block b reads bytes [per * b, per * (b + 1)) of p (per a multiple of 16
+// of at most NL * 4096: up to NL loads of 16 bytes per lane, a lane past the
+// block's bytes re-reading its first 16, which adds no HBM traffic) and, when
+// p2 is not null, bytes [per2 * b, per2 * (b + 1)) of p2 (per2 <= 4096, a
+// multiple of 16, the same way).
 template <int NL>
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, const uint8_t* p2, uint32_t per2,
-                                                          uint32_t* sink) {
-  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p + size_t(blockIdx.x) * (NL * 4096)) + threadIdx.x;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, uint32_t per, const uint8_t* p2,
+                                                          uint32_t per2, uint32_t* sink) {
+  const uint8_t* base = p + size_t(blockIdx.x) * per;
   u32x4_t v[NL + 1];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) v[i] = q[256 * i];
+  for (int i = 0; i < NL; ++i) {
+    const uint32_t o = 16 * (threadIdx.x + 256 * i);
+    v[i] = *reinterpret_cast<const u32x4_t*>(base + (o < per ? o : 0));
+  }
   v[NL] = u32x4_t{0u, 0u, 0u, 0u};
   if (p2) {
     const uint32_t o = 16 * threadIdx.x < per2 ? 16 * threadIdx.x : 0;
@@ -53,7 +57,7 @@ int mlaqdiag_empty(int grid, void* sink, void* stream) {
 }
 
 // Enqueue a read of `bytes` bytes at `p` in `grid` blocks of 256 threads
-// (bytes / grid must be 4096, 8192, 12288 or 16384), plus `bytes2` bytes at
+// (bytes / grid a multiple of 16 of at most 16384), plus `bytes2` bytes at
 // `p2` spread over the same blocks (p2 may be null with bytes2 = 0;
 // otherwise bytes2 / grid must be a multiple of 16 of at most 4096). Both
 // pointers 16-byte aligned. Returns 0 or a hipError_t value.
@@ -66,16 +70,17 @@ int mlaqdiag_read_grid(const void* p, size_t bytes, const void* p2, size_t bytes
          : bytes2 != 0)
     return int(hipErrorInvalidValue);
   const size_t per = bytes / size_t(grid);
-  const void* fn = per == 4096    ? reinterpret_cast<const void*>(&stream_read_kernel<1>)
-                   : per == 8192  ? reinterpret_cast<const void*>(&stream_read_kernel<2>)
-                   : per == 12288 ? reinterpret_cast<const void*>(&stream_read_kernel<3>)
-                   : per == 16384 ? reinterpret_cast<const void*>(&stream_read_kernel<4>)
-                                  : nullptr;
-  if (!fn) return int(hipErrorInvalidValue);
+  if (per == 0 || per % 16 != 0 || per > 16384) return int(hipErrorInvalidValue);
+  const int nl = int((per + 4095) / 4096);
+  const void* fn = nl == 1   ? reinterpret_cast<const void*>(&stream_read_kernel<1>)
+                   : nl == 2 ? reinterpret_cast<const void*>(&stream_read_kernel<2>)
+                   : nl == 3 ? reinterpret_cast<const void*>(&stream_read_kernel<3>)
+                             : reinterpret_cast<const void*>(&stream_read_kernel<4>);
   const uint8_t* pp = static_cast<const uint8_t*>(p);
   const uint8_t* pp2 = static_cast<const uint8_t*>(p2);
+  uint32_t per32 = uint32_t(per);
   uint32_t per2 = uint32_t(p2 ? bytes2 / size_t(grid) : 0);
-  void* args[] = {&pp, &pp2, &per2, &sink};
+  void* args[] = {&pp, &per32, &pp2, &per2, &sink};
   return int(hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
 }
 
