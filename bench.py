@@ -24,7 +24,9 @@ Printed JSON line (stdout, one line):
               cold launches, against the 8 TB/s HBM peak
   per_call_cold the metric per call on cold weights: H=16, M in {1,2,4,8,16,32},
               BF16 and MXFP8 weights, BF16 and E4M3 output, us per call, GB/s
-              and roofline fraction, beside same-grid floors per weight format
+              and roofline fraction, beside same-grid floors per weight format;
+              under "heads" the same for H=8 M=1 and H=11 M in {1,3,7,16,32}
+              (BF16 weights and output), each beside its own grid's floors
   per_call_warm warm-cache us per call for H=16, M in {1,2,4,8,16,32}, BF16 and
               MXFP8 weights (BF16 output), plus H=8 M=1 and H=11 M in
               {1,3,7,16,32} (BF16), with the staged torch baseline
@@ -410,6 +412,56 @@ def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
             res["floors"][wname] = f
             log(f"[bench] per-call cold {wname} W floors ({f['grid']} workgroups): empty kernel "
                 f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us")
+    res["heads"] = other_heads_cold(torch, mq, wl, args, layers, copies, stream, diag)
+    return res
+
+
+def other_heads_cold(torch, mq, wl, args, layers, copies, stream, diag):
+    """The smallest case (H = 8, M = 1) and the odd head count (H = 11,
+    M = 1/3/7/16/32) per call on cold weights, BF16 weights and output: the
+    head slices [0, Hc) and [16 - Hc, 16) of the 32 BF16 layers' weight copies
+    give 12 graphs of 32 calls, replayed round-robin (384 MiB of distinct
+    weights, so every call reads its slab from HBM), streaming hint; each
+    shape beside its same-grid floors (empty kernel; pure read of the slab)."""
+    bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
+    res = {}
+    for name, hc, ms in (("h8", 8, (1,)), ("h11", 11, (1, 3, 7, 16, 32))):
+        sets = [[copies[c][i][0][lo:lo + hc] for i in bf] for c in range(COPIES) for lo in (0, H - hc)]
+        qp = {i: (layers[i].q[:, :hc].contiguous(), layers[i].pe[:, :hc].contiguous()) for i in bf}
+        outs = {i: torch.empty((M_STEP, hc, mq.ROW), dtype=torch.bfloat16, device="cuda") for i in bf}
+        mq.mlaq_prewarm(hc, list(ms), mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+        row = {"H": hc, "graphs": len(sets), "bf16_out": {}, "floors": {}}
+        for M in ms:
+            graphs = []
+            for ws in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(stream):
+                    with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                        for w, i in zip(ws, bf):
+                            q, pe = qp[i]
+                            mq.mlaq_run_ex(q[:M], pe[:M], w, None, None, outs[i][:M], mq.MLAQ_WEIGHT_BF16,
+                                           mq.MLAQ_OUT_BF16, cache_hint=mq.MLAQ_CACHE_STREAM)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
+            nbytes = wl.algorithmic_bytes(M, hc, mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            row["bf16_out"][str(M)] = {"us": round(us, 4), "gbs": round(gbs, 1),
+                                       "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+            log(f"[bench] per-call cold bf16 W, bf16_out, H={hc} M={M}: {us:.3f} us, {gbs:.1f} GB/s "
+                f"({gbs / HBM_PEAK_GBS:.4f} of peak)")
+            del graphs
+        if diag is not None:
+            # The kernel's grid: 16-column tiles at H = 8 with one token tile,
+            # 32-column tiles otherwise (one workgroup per head and tile).
+            grids = sorted({hc * (mq.LATENT_DIM // (16 if hc == 8 and M <= 16 else 32)) for M in ms})
+            for grid in grids:
+                f = shape_floors(torch, diag, grid, [[(w, None) for w in ws] for ws in sets], stream,
+                                 args.steps, args.warmup)
+                row["floors"][str(grid)] = f
+                log(f"[bench] per-call cold H={hc} floors ({grid} workgroups): empty kernel "
+                    f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us")
+        res[name] = row
     return res
 
 

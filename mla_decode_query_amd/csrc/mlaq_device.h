@@ -59,32 +59,45 @@ __device__ __forceinline__ uint32_t e4m3x4_satfinite(float v0, float v1, float v
   return uint32_t(r);
 }
 
-// Correctly rounded fp32 quotient y / b from rb = RN(1/b): q0 = RN(y * rb)
-// is within one ulp of y / b, the residual y - q0 * b is exact in one FMA,
-// and one FMA correction then gives RN(y / b) (Markstein's correction step).
-// Checked against IEEE division for every finite bf16 y and 40,000 divisors
-// with 2^-64 <= |b| < 2^65. Valid while rb is a normal number; for
-// |y| < 2^-100 the residual can underflow, and q0 (which carries the sign)
-// is returned. Callers that encode the quotient to E4M3 use it only for
-// divisors accepted by div_rn_covers.
-__device__ __forceinline__ float div_rn(float y, float b, float rb) {
-  const float q0 = y * rb;
-  const float rho = __builtin_fmaf(-q0, b, y);
+// The E4M3 epilogue's quotient, from rb = RN(1/b) and lim = RN(448 |b|)
+// (both once per call), for divisors accepted by quot_e4m3_covers. Returns a
+// value whose plain E4M3 conversion (e4m3x4_in_range) is the code of
+// e4m3_satfinite(RN(y / b)) for every y:
+//  - y is first clamped to [-lim, lim] with IEEE maximum/minimum, which keep
+//    NaN (an infinite y becomes +-lim). A clamped quotient lies within a few
+//    ulp of +-448 and encodes to +-448, as every quotient past 448 does under
+//    saturation, and no quotient left can round past 448, so the convert
+//    needs no clamp of its own;
+//  - q0 = RN(y * rb) is within one ulp of y / b, the residual y - q0 * b is
+//    exact in one FMA, and one FMA correction gives RN(y / b) (Markstein's
+//    correction step);
+//  - for |y| < 2^-100 the residual may underflow, but the quotient is then
+//    at most 2^-10 in magnitude and encodes to a zero; its sign is that of
+//    q0, which the final sign copy restores (the correction alone can turn
+//    -0 into +0).
+__device__ __forceinline__ float quot_e4m3(float y, float b, float rb, float lim) {
+  const float yc = __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -lim), lim);
+  const float q0 = yc * rb;
+  const float rho = __builtin_fmaf(-q0, b, yc);
   const float q1 = __builtin_fmaf(rho, rb, q0);
-  // q0 is the answer when it is not finite (overflow, NaN) and for tiny or
-  // zero y (which also keeps the sign of a zero quotient).
-  const bool plain = !(__builtin_fabsf(y) >= 0x1p-100f) || !(__builtin_fabsf(q0) <= 0x1.fffffep127f);
-  return plain ? q0 : q1;
+  return __builtin_copysignf(q1, q0);
 }
 
-// Divisors for which div_rn followed by the E4M3 encoder gives the code of
-// the IEEE quotient for every y: 1/b is then a normal fp32, and a quotient of
-// |y| < 2^-100 stays at most 2^-10, which encodes to a signed zero whether or
-// not its last bit is right. Others (0, subnormal or huge b, inf, NaN) take
-// the IEEE division.
-__device__ __forceinline__ bool div_rn_covers(float b) {
+// Divisors for which quot_e4m3 holds: 1/b is a normal fp32, 448 |b| is
+// finite, and a quotient of |y| < 2^-100 stays at most 2^-10. Others (0,
+// subnormal or huge b, inf, NaN) take the IEEE division and the saturating
+// encoder.
+__device__ __forceinline__ bool quot_e4m3_covers(float b) {
   const float ab = __builtin_fabsf(b);
-  return ab >= 0x1p-90f && ab <= 0x1p126f;
+  return ab >= 0x1p-90f && ab <= 0x1p118f;
+}
+
+// Four values in E4M3 range (|v| rounds to at most 448, or NaN) -> four OCP
+// E4M3FN codes, round to nearest even.
+__device__ __forceinline__ uint32_t e4m3x4_in_range(float v0, float v1, float v2, float v3) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, r, true);
+  return uint32_t(r);
 }
 
 // E8M0 scale byte s as the scale operand of the scaled convert below: the

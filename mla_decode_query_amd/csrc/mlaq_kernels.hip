@@ -189,15 +189,20 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  float qs = 1.0f, rqs = 1.0f;
+  float qs = 1.0f, rqs = 1.0f, lim = 0.0f;
   if constexpr (OF == MLAQ_OUT_E4M3) {
     qs = *a.q_scale;
     rqs = 1.0f / qs;
+    lim = 448.0f * __builtin_fabsf(qs);
   }
   auto tail = [&](auto ieee_div) __attribute__((always_inline)) {
-    auto quot = [&](float (&x)[4]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = decltype(ieee_div)::value ? x[c] / qs : div_rn(x[c], qs, rqs);
+    // Four values -> their E4M3 codes e4m3_satfinite(RN(x / q_scale)).
+    auto encode = [&](float x0, float x1, float x2, float x3) __attribute__((always_inline)) {
+      if constexpr (decltype(ieee_div)::value)
+        return e4m3x4_satfinite(x0 / qs, x1 / qs, x2 / qs, x3 / qs);
+      else
+        return e4m3x4_in_range(quot_e4m3(x0, qs, rqs, lim), quot_e4m3(x1, qs, rqs, lim),
+                               quot_e4m3(x2, qs, rqs, lim), quot_e4m3(x3, qs, rqs, lim));
     };
     // 4. q_pe into columns 512..575. Loads and stores share one counter of
     //    outstanding memory operations, so a store issued before the last
@@ -213,14 +218,11 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
       if constexpr (OF == MLAQ_OUT_BF16) {
         store_out<NT>(at_byte<u32x4_t>(a.out, 2 * pe_o), pe_v);
       } else {
-        float x[2][4];
+        float x[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          x[c >> 2][c & 3] = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
-        quot(x[0]);
-        quot(x[1]);
-        pe_e4[0] = e4m3x4_satfinite(x[0][0], x[0][1], x[0][2], x[0][3]);
-        pe_e4[1] = e4m3x4_satfinite(x[1][0], x[1][1], x[1][2], x[1][3]);
+        for (int c = 0; c < 8; ++c) x[c] = __uint_as_float(((pe_v[c >> 1] >> (16 * (c & 1))) & 0xffffu) << 16);
+        pe_e4[0] = encode(x[0], x[1], x[2], x[3]);
+        pe_e4[1] = encode(x[4], x[5], x[6], x[7]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -302,15 +304,14 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
       if constexpr (OF == MLAQ_OUT_BF16) {
         store_out<NT>(at_byte<u32x2_t>(a.out, 2 * o), u32x2_t{b01, b23});
       } else {
-        float y[4] = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u), __uint_as_float(b23 << 16),
-                      __uint_as_float(b23 & 0xffff0000u)};
-        quot(y);
-        store_out<NT>(at_byte<uint32_t>(a.out, o), e4m3x4_satfinite(y[0], y[1], y[2], y[3]));
+        store_out<NT>(at_byte<uint32_t>(a.out, o),
+                      encode(__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u),
+                             __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)));
       }
     }
   };
   if constexpr (OF == MLAQ_OUT_E4M3) {
-    if (__builtin_expect(div_rn_covers(qs), 1))
+    if (__builtin_expect(quot_e4m3_covers(qs), 1))
       tail(Flag<false>{});
     else
       tail(Flag<true>{});

@@ -9,13 +9,17 @@
 // and "Safety scope and PR 173"; the widths are readings.)
 //
 // Layout makes the MFMA easy: the reduction axis (latent c) is contiguous in
-// memory, so a lane's 16-byte load of 8 consecutive c of one value column is
-// directly its B fragment for v_mfma_f32_16x16x32_bf16 (element e of lane
-// j + 16g = row c0 + 8g + e of column j), and the A fragment is the same
-// 8 c of token j's x row. A workgroup (4 waves) owns one head, CB value
-// columns and one 16-token tile; wave w reduces c in [128w, 128w+128) over
-// four MFMAs, and the four partial tiles are summed through LDS in a fixed
-// order. Every workgroup reads its head's x rows for its tile from L2, which
+// memory, so a lane's load of 8 consecutive c of one value column is
+// directly its B fragment for v_mfma_f32_16x16x32_bf16, and the A fragment
+// is the same 8 c of token j's x row. The MFMA sums element e of lane
+// j + 16g of A against element e of lane i + 16g of B over all g and e, so
+// any assignment of c to (g, e) that A and B share is valid: lane (j, g) of
+// wave w takes the 32 consecutive c in [128w + 32g, 128w + 32g + 32), one
+// MX scale group, 8 per MFMA k-block kb (c = 128w + 32g + 8kb + e). Its
+// weights are then 64 (BF16) or 32 (E4M3) contiguous bytes and, for MXFP8,
+// one scale byte. A workgroup (4 waves) owns one head, CB value columns and
+// one 16-token tile; wave w reduces c in [128w, 128w+128) over four MFMAs,
+// and the four partial tiles are summed through LDS in a fixed order. Every workgroup reads its head's x rows for its tile from L2, which
 // is the per-CU traffic that grows with M, so the shape keeps 256 workgroups
 // at H = 16 either way: for M <= 16, CB = 8 (the upper 8 MFMA columns repeat
 // the lower 8 at the same addresses, so no extra HBM traffic, and are
@@ -24,10 +28,10 @@
 // two tiles of a column block on the same XCD so its weights come from HBM
 // once.
 //
-// MXFP8: a lane loads 8 E4M3 bytes and the one E8M0 byte of their 32-group;
-// v_cvt_scalef32_pk_bf16_fp8 gives the exact bf16 of each byte times
-// 2^(S-127), so the MFMA forms exact products as the oracle's dequantization
-// does.
+// MXFP8: a lane loads its 32 E4M3 bytes (two 16-byte loads) and the one
+// E8M0 byte of their group; v_cvt_scalef32_pk_bf16_fp8 gives the exact bf16
+// of each byte times 2^(S-127), so the MFMA forms exact products as the
+// oracle's dequantization does.
 #include "mlaq.h"
 #include "mlaq_device.h"
 #include "mlaq_internal.h"
@@ -68,30 +72,30 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   const int vb = hr / NMT, mt = hr - (hr / NMT) * NMT;
   const int v = vb * CB + (j % CB); // this lane's value column
   const int M = a.M, H = a.H;
-  const int cbase = 128 * wave + 8 * g; // + 32 kb: this lane's 8 latent values per MFMA
+  const int cbase = 128 * wave + 32 * g; // + 8 kb: this lane's 8 latent values per MFMA
 
-  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values.
+  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values, all 32
+  //    contiguous in the W_UV row.
   u32x4_t wb[4];
-  uint32_t sc[4];
+  uint32_t sc = 0;
   if constexpr (WF == MLAQ_WEIGHT_BF16) {
     const uint32_t off = ((uint32_t(h) * kValue + v) * kLatent + cbase) * 2;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if constexpr (NT)
-        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 64 * kb));
+        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 16 * kb));
       else
-        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 64 * kb);
+        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 16 * kb);
     }
   } else {
-    u32x2_t w8[4];
     const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) w8[kb] = *at_byte<const u32x2_t>(a.w, off + 32 * kb);
-    const uint32_t soff = (uint32_t(h) * kValue + v) * kUvScalesPerRow + cbase / kMxBlock;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sc[kb] = a.w_scales[soff + kb];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) wb[kb] = u32x4_t{w8[kb][0], w8[kb][1], 0u, 0u}; // decoded below
+    const u32x4_t w0 = *at_byte<const u32x4_t>(a.w, off);
+    const u32x4_t w1 = *at_byte<const u32x4_t>(a.w, off + 16);
+    sc = a.w_scales[(uint32_t(h) * kValue + v) * kUvScalesPerRow + cbase / kMxBlock];
+    wb[0] = u32x4_t{w0[0], w0[1], 0u, 0u}; // decoded below
+    wb[1] = u32x4_t{w0[2], w0[3], 0u, 0u};
+    wb[2] = u32x4_t{w1[0], w1[1], 0u, 0u};
+    wb[3] = u32x4_t{w1[2], w1[3], 0u, 0u};
   }
 
   // 2. A fragments: token 16 mt + j, the same 8 latent values per k-block.
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
     const int mc = m < M ? m : 0;
     const uint32_t off = ((uint32_t(mc) * H + h) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 64 * kb);
+    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 16 * kb);
   }
   __builtin_amdgcn_sched_barrier(0); // every load is in flight before any wait
 
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
     if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
       // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16
       // pairs, one scaled conversion each.
-      const float s = e8m0_scale_operand(sc[kb]);
+      const float s = e8m0_scale_operand(sc);
       u32x4_t d;
 #pragma unroll
       for (int p = 0; p < 4; ++p) d[p] = e4m3x2_scaled_bf16(b[p >> 1], s, p & 1);

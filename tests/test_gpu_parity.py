@@ -253,12 +253,14 @@ def test_e4m3_decode_every_scale_byte():
 
 @pytest.mark.parametrize("q_scale", [
     1.0, 0.125, 3.0, 1.0 / 448, -0.75,
-    # The edges of the range where the kernel divides with one FMA correction
-    # of x * RN(1/q_scale), and scales outside it (IEEE division there): a
-    # subnormal scale whose reciprocal overflows, the smallest normal, huge
-    # scales with subnormal reciprocals, zero, inf and NaN.
-    2.0 ** -90, 3 * 2.0 ** -95, 3 * 2.0 ** -140, 2.0 ** -126, 2.0 ** -127, 2.0 ** 126, 1.5 * 2.0 ** 127,
-    0.0, float("inf"), float("nan"),
+    # The edges of the range where the kernel clamps x to 448 |q_scale| and
+    # divides with one FMA correction of x * RN(1/q_scale) (2^-90 <= |q_scale|
+    # <= 2^118), and scales outside it (IEEE division there): a subnormal
+    # scale whose reciprocal overflows, the smallest normal, scales whose
+    # 448-multiple overflows, huge scales with subnormal reciprocals, zero,
+    # inf and NaN.
+    2.0 ** -90, 3 * 2.0 ** -95, -(2.0 ** 118), 1.25 * 2.0 ** 118, 1.5 * 2.0 ** 119, 3 * 2.0 ** -140,
+    2.0 ** -126, 2.0 ** -127, 2.0 ** 126, 1.5 * 2.0 ** 127, 0.0, float("inf"), float("nan"),
 ])
 def test_e4m3_encode_exhaustive_via_q_pe(q_scale):
     """All 65536 bf16 patterns through the q_pe lanes of E4M3 output:
