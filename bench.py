@@ -304,6 +304,8 @@ def diag_lib():
     P = ctypes.c_void_p
     diag.mlaqdiag_empty.argtypes = [ctypes.c_int, P, P]
     diag.mlaqdiag_read_grid.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, ctypes.c_int, P, P]
+    diag.mlaqdiag_read_store_grid.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, ctypes.c_int, ctypes.c_size_t,
+                                              ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
     return diag
 
 
@@ -358,8 +360,35 @@ def floors_leg(torch, mq, layers, copies, stream, args):
     f = shape_floors(torch, diag, 256, [[copies[c][i] for i in bf] for c in range(COPIES)], stream, args.steps,
                      args.warmup)
     log(f"[bench] floors: empty kernel {f['empty_kernel_us']:.3f} us/node, cold 2 MiB read {f['cold_read_us']:.3f} us/node")
+    # Read and store: the same reads, then the dominant kernel's E4M3 output
+    # rows ([32,16,576], 32 bytes per row and tile, 8 threads per row) stored
+    # in its epilogue's pattern once the loads arrive, into buffers of its own.
+    outs = [torch.empty((M_STEP, H, mq.ROW), dtype=torch.uint8, device="cuda") for _ in bf]
+
+    def rs_body_for(c):
+        def body():
+            st = torch.cuda.current_stream().cuda_stream
+            for i, o in zip(bf, outs):
+                w, _ = copies[c][i]
+                assert diag.mlaqdiag_read_store_grid(w.data_ptr(), w.numel() * w.element_size(), o.data_ptr(),
+                                                     o.numel(), M_STEP, H * mq.ROW, mq.ROW, mq.LATENT_DIM // 32, 4,
+                                                     256, st) == 0
+        return body
+
+    graphs = []
+    for c in range(COPIES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                rs_body_for(c)()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    rs_us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
+    log(f"[bench] floors: cold 2 MiB read + the E4M3 output stores {rs_us:.3f} us/node")
     return {"empty_kernel_us": f["empty_kernel_us"], "cold_read_2MiB_us": f["cold_read_us"],
-            "note": "per graph node, same grid as the dominant kernel; the read kernel moves the same weight bytes"}
+            "cold_read_store_us": round(rs_us, 4),
+            "note": "per graph node, same grid as the dominant kernel; the read kernel moves the same weight bytes, "
+                    "the read-store kernel also stores the same E4M3 output bytes in the epilogue's pattern"}
 
 
 def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):

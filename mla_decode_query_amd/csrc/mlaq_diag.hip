@@ -1,10 +1,12 @@
 // mlaq_diag.hip -- measurement floors for the benchmark (libmlaq_diag.so).
 // Not part of the fused path. The kernels give the cost of a launch shape
-// itself in a hipGraph: one that does nothing, and one that streams given
-// byte ranges in as many blocks as the measured kernel has workgroups (each
-// block reads its contiguous share, 16 bytes per lane per load, every load
-// issued before any wait) and writes nothing. Their per-node times are the
-// floors a fused kernel of that grid is compared against.
+// itself in a hipGraph: one that does nothing, one that streams given byte
+// ranges in as many blocks as the measured kernel has workgroups (each block
+// reads its contiguous share, 16 bytes per lane per load, every load issued
+// before any wait) and writes nothing, and one that also stores the fused
+// kernel's output bytes in its epilogue's pattern once the loads arrive.
+// Their per-node times are the floors a fused kernel of that grid is
+// compared against.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -12,6 +14,7 @@
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void empty_kernel(uint32_t* sink) {
   if (threadIdx.x == 0xffffu) sink[0] = 1u; // never true: keeps the kernel non-empty for the compiler
@@ -41,6 +44,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, uint
 #pragma unroll
   for (int i = 0; i <= NL; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
   if (x == 0x9e3779b9u && threadIdx.x == 0) sink[0] = x; // data-dependent, practically never taken
+}
+
+// The read above followed by stores in the fused kernel's epilogue pattern:
+// block b (tile b: head b / tiles_per_head, column tile b % tiles_per_head)
+// has thread t write SB bytes at row t / 8, column group t % 8 of its tile
+// (8 threads per row, so 8 SB contiguous bytes per row and tile) for rows
+// below `rows`, once its loads have arrived (the stored words depend on the
+// loaded data). No arithmetic beyond that.
+template <int NL, int SB>
+__global__ __launch_bounds__(256) void read_store_kernel(const uint8_t* p, uint32_t per, uint8_t* out, uint32_t rows,
+                                                         uint32_t tiles_per_head, uint32_t row_stride,
+                                                         uint32_t head_stride) {
+  const uint8_t* base = p + size_t(blockIdx.x) * per;
+  u32x4_t v[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const uint32_t o = 16 * (threadIdx.x + 256 * i);
+    v[i] = *reinterpret_cast<const u32x4_t*>(base + (o < per ? o : 0));
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+  const uint32_t row = threadIdx.x / 8, grp = threadIdx.x % 8;
+  if (row < rows) {
+    const uint32_t h = blockIdx.x / tiles_per_head, ct = blockIdx.x % tiles_per_head;
+    uint8_t* dst = out + size_t(row) * row_stride + size_t(h) * head_stride + (ct * 8 + grp) * SB;
+    if constexpr (SB == 4)
+      *reinterpret_cast<uint32_t*>(dst) = x;
+    else
+      *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{x, x ^ 1u};
+  }
 }
 
 } // namespace
@@ -81,6 +115,40 @@ int mlaqdiag_read_grid(const void* p, size_t bytes, const void* p2, size_t bytes
   uint32_t per32 = uint32_t(per);
   uint32_t per2 = uint32_t(p2 ? bytes2 / size_t(grid) : 0);
   void* args[] = {&pp, &per32, &pp2, &per2, &sink};
+  return int(hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
+}
+
+// Enqueue the read of mlaqdiag_read_grid (`bytes` at `p` in `grid` blocks,
+// bytes / grid a multiple of 16 of at most 8192) followed by the epilogue's
+// stores: `rows` rows of 8 * store_bytes bytes per block (store_bytes 4 or
+// 8, rows at most 32) into `out` (out_bytes long, 8-byte aligned), block b
+// writing at row * row_stride + (b / tiles_per_head) * head_stride +
+// (b % tiles_per_head) * 8 * store_bytes. Every store must fall inside out:
+// checked here. Returns 0 or a hipError_t value.
+int mlaqdiag_read_store_grid(const void* p, size_t bytes, void* out, size_t out_bytes, int rows, size_t row_stride,
+                             size_t head_stride, int tiles_per_head, int store_bytes, int grid, void* stream) {
+  if (!p || !out || grid < 1 || tiles_per_head < 1 || grid % tiles_per_head != 0 || rows < 1 || rows > 32 ||
+      (store_bytes != 4 && store_bytes != 8) || bytes % size_t(grid) != 0 ||
+      (reinterpret_cast<uintptr_t>(p) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 7) != 0 ||
+      row_stride % size_t(store_bytes) != 0 || head_stride % size_t(store_bytes) != 0 || row_stride > 0xffffffffu ||
+      head_stride > 0xffffffffu)
+    return int(hipErrorInvalidValue);
+  const size_t per = bytes / size_t(grid);
+  if (per == 0 || per % 16 != 0 || per > 8192) return int(hipErrorInvalidValue);
+  const size_t heads = size_t(grid / tiles_per_head);
+  const size_t last = size_t(rows - 1) * row_stride + (heads - 1) * head_stride +
+                      size_t(tiles_per_head) * 8 * size_t(store_bytes);
+  if (last > out_bytes) return int(hipErrorInvalidValue);
+  const int nl = int((per + 4095) / 4096);
+  const void* fn = store_bytes == 4 ? (nl == 1 ? reinterpret_cast<const void*>(&read_store_kernel<1, 4>)
+                                               : reinterpret_cast<const void*>(&read_store_kernel<2, 4>))
+                                    : (nl == 1 ? reinterpret_cast<const void*>(&read_store_kernel<1, 8>)
+                                               : reinterpret_cast<const void*>(&read_store_kernel<2, 8>));
+  const uint8_t* pp = static_cast<const uint8_t*>(p);
+  uint8_t* po = static_cast<uint8_t*>(out);
+  uint32_t per32 = uint32_t(per), rows32 = uint32_t(rows), tph = uint32_t(tiles_per_head);
+  uint32_t rs = uint32_t(row_stride), hs = uint32_t(head_stride);
+  void* args[] = {&pp, &per32, &po, &rows32, &tph, &rs, &hs};
   return int(hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
 }
 

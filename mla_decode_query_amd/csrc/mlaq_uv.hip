@@ -13,11 +13,15 @@
 // directly its B fragment for v_mfma_f32_16x16x32_bf16, and the A fragment
 // is the same 8 c of token j's x row. The MFMA sums element e of lane
 // j + 16g of A against element e of lane i + 16g of B over all g and e, so
-// any assignment of c to (g, e) that A and B share is valid: lane (j, g) of
-// wave w takes the 32 consecutive c in [128w + 32g, 128w + 32g + 32), one
-// MX scale group, 8 per MFMA k-block kb (c = 128w + 32g + 8kb + e). Its
-// weights are then 64 (BF16) or 32 (E4M3) contiguous bytes and, for MXFP8,
-// one scale byte. A workgroup (4 waves) owns one head, CB value columns and
+// any assignment of c to (g, e) that A and B share is valid. BF16 weights:
+// lane (j, g) of wave w takes c = 128w + 32kb + 8g + e in k-block kb, so one
+// load instruction covers 64 contiguous bytes of each of 16 rows. MXFP8
+// weights: the lane takes the 32 consecutive c in [128w + 32g, +32), one MX
+// scale group, 8 per k-block (c = 128w + 32g + 8kb + e): two 16-byte loads
+// and one scale byte per lane instead of four 8-byte loads and their scale
+// bytes. (The grouped form made cold BF16 launches with nontemporal loads
+// about 10% longer: each instruction then touches every 128-byte line of a
+// row segment in 16-byte pieces.) A workgroup (4 waves) owns one head, CB value columns and
 // one 16-token tile; wave w reduces c in [128w, 128w+128) over four MFMAs,
 // and the four partial tiles are summed through LDS in a fixed order. Every workgroup reads its head's x rows for its tile from L2, which
 // is the per-CU traffic that grows with M, so the shape keeps 256 workgroups
@@ -72,10 +76,12 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   const int vb = hr / NMT, mt = hr - (hr / NMT) * NMT;
   const int v = vb * CB + (j % CB); // this lane's value column
   const int M = a.M, H = a.H;
-  const int cbase = 128 * wave + 32 * g; // + 8 kb: this lane's 8 latent values per MFMA
+  // This lane's first latent value, and the step between its k-blocks.
+  constexpr bool kGrouped = WF == MLAQ_WEIGHT_MXFP8;
+  constexpr int kStep = kGrouped ? 8 : 32;
+  const int cbase = 128 * wave + (kGrouped ? 32 : 8) * g;
 
-  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values, all 32
-  //    contiguous in the W_UV row.
+  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values.
   u32x4_t wb[4];
   uint32_t sc = 0;
   if constexpr (WF == MLAQ_WEIGHT_BF16) {
@@ -83,9 +89,9 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if constexpr (NT)
-        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 16 * kb));
+        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb));
       else
-        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 16 * kb);
+        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb);
     }
   } else {
     const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
     const int mc = m < M ? m : 0;
     const uint32_t off = ((uint32_t(mc) * H + h) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 16 * kb);
+    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 2 * kStep * kb);
   }
   __builtin_amdgcn_sched_barrier(0); // every load is in flight before any wait
 
