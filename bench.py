@@ -394,25 +394,32 @@ def floors_leg(torch, mq, layers, copies, stream, args):
 def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
     """The metric per call, cold: for H = 16, each weight format, each output
     dtype and M in {1,2,4,8,16,32}, the 32 layers of that format back to back
-    in one hipGraph per weight copy, the 6 copies replayed round-robin (every
+    in one hipGraph per weight copy, the copies replayed round-robin (over
+    400 MB of weights per format, above the 256 MB Infinity Cache, so every
     layer's weights come from HBM), with the streaming cache hint; us per
     call, algorithmic GB/s and the fraction of the 8 TB/s HBM peak, beside
     the same-grid floors of each weight format (empty kernel; pure read of
     the layer's weight bytes)."""
     out_bf = {i: torch.empty((M_STEP, H, mq.ROW), dtype=torch.bfloat16, device="cuda") for i in range(len(layers))}
-    res = {"H": H, "layers_per_graph": None, "copies": COPIES, "cache_hint": "stream", "floors": {}}
+    res = {"H": H, "layers_per_graph": None, "copies": {}, "cache_hint": "stream", "floors": {}}
     diag = diag_lib()
     for wf, wname in ((mq.MLAQ_WEIGHT_BF16, "bf16"), (mq.MLAQ_WEIGHT_MXFP8, "mxfp8")):
         sel = [i for i, L in enumerate(layers) if L.wf == wf]
         res["layers_per_graph"] = len(sel)
         res[wname] = {}
+        # One graph per weight copy. The 32 MXFP8 layers of the step's 6 copies
+        # (207 MB) would fit in the 256 MB Infinity Cache, so MXFP8 gets 6 more
+        # copies of its own (414 MB); BF16's 6 copies hold 402 MB.
+        wsets = [[copies[c][i] for i in sel] for c in range(COPIES)]
+        if wf == mq.MLAQ_WEIGHT_MXFP8:
+            wsets += [[layers[i].weights_on_device(torch, mq) for i in sel] for _ in range(COPIES)]
+        res["copies"][wname] = len(wsets)
         for od, oname in ((mq.MLAQ_OUT_BF16, "bf16_out"), (mq.MLAQ_OUT_E4M3, "e4m3_out")):
             res[wname][oname] = {}
             for M in (1, 2, 4, 8, 16, 32):
                 def body(c, M=M, od=od):
-                    for i in sel:
+                    for i, (w, s) in zip(sel, wsets[c]):
                         L = layers[i]
-                        w, s = copies[c][i]
                         if od == mq.MLAQ_OUT_BF16:
                             mq.mlaq_run_ex(L.q[:M], L.pe[:M], w, s, None, out_bf[i][:M], wf, od,
                                            cache_hint=mq.MLAQ_CACHE_STREAM)
@@ -420,7 +427,7 @@ def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
                             mq.mlaq_run_ex(L.q[:M], L.pe[:M], w, s, L.qs, L.out[:M], wf, od,
                                            cache_hint=mq.MLAQ_CACHE_STREAM)
                 graphs = []
-                for c in range(COPIES):
+                for c in range(len(wsets)):
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.stream(stream):
                         with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
@@ -436,8 +443,7 @@ def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
                     f"({gbs / HBM_PEAK_GBS:.4f} of peak)")
                 del graphs
         if diag is not None:
-            f = shape_floors(torch, diag, H * 16, [[copies[c][i] for i in sel] for c in range(COPIES)], stream,
-                             args.steps, args.warmup)
+            f = shape_floors(torch, diag, H * 16, wsets, stream, args.steps, args.warmup)
             res["floors"][wname] = f
             log(f"[bench] per-call cold {wname} W floors ({f['grid']} workgroups): empty kernel "
                 f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us")
@@ -449,13 +455,15 @@ def other_heads_cold(torch, mq, wl, args, layers, copies, stream, diag):
     """The smallest case (H = 8, M = 1) and the odd head count (H = 11,
     M = 1/3/7/16/32) per call on cold weights, BF16 weights and output: the
     head slices [0, Hc) and [16 - Hc, 16) of the 32 BF16 layers' weight copies
-    give 12 graphs of 32 calls, replayed round-robin (384 MiB of distinct
-    weights, so every call reads its slab from HBM), streaming hint; each
-    shape beside its same-grid floors (empty kernel; pure read of the slab)."""
+    give 12 graphs of 32 calls, replayed round-robin, all copies' first slices
+    before any second slice (384 MiB of distinct weights; at H = 11 the heads
+    both slices share come back after six graphs, 264 MiB of other weights),
+    so every call reads its slab from HBM; streaming hint; each shape beside
+    its same-grid floors (empty kernel; pure read of the slab)."""
     bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
     res = {}
     for name, hc, ms in (("h8", 8, (1,)), ("h11", 11, (1, 3, 7, 16, 32))):
-        sets = [[copies[c][i][0][lo:lo + hc] for i in bf] for c in range(COPIES) for lo in (0, H - hc)]
+        sets = [[copies[c][i][0][lo:lo + hc] for i in bf] for lo in (0, H - hc) for c in range(COPIES)]
         qp = {i: (layers[i].q[:, :hc].contiguous(), layers[i].pe[:, :hc].contiguous()) for i in bf}
         outs = {i: torch.empty((M_STEP, hc, mq.ROW), dtype=torch.bfloat16, device="cuda") for i in bf}
         mq.mlaq_prewarm(hc, list(ms), mq.MLAQ_WEIGHT_BF16, mq.MLAQ_OUT_BF16)
