@@ -36,9 +36,14 @@
 //    batch calls, 2.9% at 64k, than issuing them after it) and every tile has
 //    a whole iteration of compute to arrive; its page indices are fetched one
 //    tile earlier still;
-//  - online softmax in the log2 domain: the row max over the tile is reduced
-//    across the 16 lanes of a row with DPP and across the 4 waves through
-//    LDS; the running sums stay per lane until the end;
+//  - online softmax in the log2 domain, against a reference maximum that
+//    moves only when a score exceeds it by more than 8 (weights up to 2^8,
+//    exact in fp32, in range for bf16): a tile then needs no exchange of row
+//    maxima before its weights, one workgroup barrier fewer (0.7% shorter
+//    decode batch calls, 1.1% at 64k); when a wave sees such a score (always
+//    on the first tile), the reference moves to the tile's row maximum, whose
+//    wave parts (DPP within rows) are published in LDS beside the flags; the
+//    running sums stay per lane until the end;
 //  - P (bf16; for FP32 partials also its bf16 remainder, so that P enters
 //    the value product with 16 significant bits) goes to LDS; wave w
 //    multiplies it by the value columns
@@ -76,6 +81,7 @@ static_assert(16 * kQPitch <= kTileBytes, "query staging fits the tile");
 constexpr int kPPitch = kAttnTile + 8;      // bf16 per head row of the LDS P tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRefSlack = 8.f; // log2 of the largest softmax weight allowed against a stale reference
 
 constexpr int kPartialBf16 = MLAQ_PARTIAL_BF16;
 constexpr int kPartialFp32 = MLAQ_PARTIAL_FP32;
@@ -199,6 +205,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kvt[kTileBytes]; // the current tile, row = token
   __shared__ __attribute__((aligned(16))) uint16_t pt[(kSplitP ? 2 : 1) * 16 * kPPitch]; // P (hi, lo), row = head
   __shared__ __attribute__((aligned(16))) float red[4][16];            // per-wave row max / sum
+  __shared__ __attribute__((aligned(16))) int flags[4];                // per-wave: a score above the reference
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -328,7 +335,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
       }
       sacc = s2[0] + s2[1];
     }
-    // 2. Masked scores in the log2 domain; tile max per row.
+    // 2. Masked scores in the log2 domain. The softmax weights are taken
+    //    against the reference m_run (the running maximum as of the last
+    //    tile that raised it) as long as no score exceeds it by more than
+    //    kRefSlack, so that a tile needs no exchange of row maxima before its
+    //    weights: weights up to 2^kRefSlack are exact in fp32 and in range for
+    //    bf16. A wave with a score above that raises its flag; if any wave
+    //    did (always on the first tile), the reference moves to the tile's
+    //    row maximum, from the wave maxima published beside the flags.
     const bool valid = t0 + trow < tb;
     float sc[4];
 #pragma unroll
@@ -337,45 +351,58 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
       const float mx = rows4_max_transposed(sc[0], sc[1], sc[2], sc[3], j);
       if (j < 4) red[w][4 * g + 2 * (j & 1) + ((j >> 1) & 1)] = mx;
     }
-    __syncthreads(); // also publishes the staged tile
-    float alpha[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      const float tmax = __builtin_fmaxf(__builtin_fmaxf(red[0][h], red[1][h]), __builtin_fmaxf(red[2][h], red[3][h]));
-      const float mn = __builtin_fmaxf(m_run[r], tmax); // finite: every tile holds a valid token
-      alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - mn);
-      m_run[r] = mn;
-      const float p = __builtin_amdgcn_exp2f(sc[r] - mn);
-      l_run[r] = l_run[r] * alpha[r] + p;
-      sc[r] = p;
-    }
+    const bool over = __any((sc[0] > m_run[0] + kRefSlack) | (sc[1] > m_run[1] + kRefSlack) |
+                            (sc[2] > m_run[2] + kRefSlack) | (sc[3] > m_run[3] + kRefSlack));
+    if (lane == 0) flags[w] = over ? 1 : 0;
     // 3. P (bf16, and for FP32 partials its bf16 remainder p - hi, exact in
-    //    fp32) into LDS in slot order; rescale the output accumulators.
-    {
-      const uint32_t p01 = bf16x2_rne(sc[0], sc[1]), p23 = bf16x2_rne(sc[2], sc[3]);
+    //    fp32) into LDS in slot order.
+    auto put_p = [&](const float (&pv)[4]) __attribute__((always_inline)) {
+      const uint32_t p01 = bf16x2_rne(pv[0], pv[1]), p23 = bf16x2_rne(pv[2], pv[3]);
       pt[(4 * g + 0) * kPPitch + pslot] = uint16_t(p01);
       pt[(4 * g + 1) * kPPitch + pslot] = uint16_t(p01 >> 16);
       pt[(4 * g + 2) * kPPitch + pslot] = uint16_t(p23);
       pt[(4 * g + 3) * kPPitch + pslot] = uint16_t(p23 >> 16);
       if constexpr (kSplitP) {
-        const uint32_t l01 = bf16x2_rne(sc[0] - __uint_as_float(p01 << 16), sc[1] - __uint_as_float(p01 & 0xffff0000u));
-        const uint32_t l23 = bf16x2_rne(sc[2] - __uint_as_float(p23 << 16), sc[3] - __uint_as_float(p23 & 0xffff0000u));
+        const uint32_t l01 = bf16x2_rne(pv[0] - __uint_as_float(p01 << 16), pv[1] - __uint_as_float(p01 & 0xffff0000u));
+        const uint32_t l23 = bf16x2_rne(pv[2] - __uint_as_float(p23 << 16), pv[3] - __uint_as_float(p23 & 0xffff0000u));
         uint16_t* plo = pt + 16 * kPPitch;
         plo[(4 * g + 0) * kPPitch + pslot] = uint16_t(l01);
         plo[(4 * g + 1) * kPPitch + pslot] = uint16_t(l01 >> 16);
         plo[(4 * g + 2) * kPPitch + pslot] = uint16_t(l23);
         plo[(4 * g + 3) * kPPitch + pslot] = uint16_t(l23 >> 16);
       }
-    }
-    // (skipped when no row maximum of this wave's rows moved: alpha is then 1)
-    if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
+    };
+    float pv[4];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+    for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(sc[r] - m_run[r]);
+    if (!over) put_p(pv);
+    __syncthreads(); // publishes the staged tile, the weights, the wave maxima and the flags
+    const int4 fl = *reinterpret_cast<const int4*>(flags);
+    if ((fl.x | fl.y | fl.z | fl.w) == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
+      for (int r = 0; r < 4; ++r) l_run[r] += pv[r];
+    } else {
+      float alpha[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * g + r;
+        const float tmax = __builtin_fmaxf(__builtin_fmaxf(red[0][h], red[1][h]), __builtin_fmaxf(red[2][h], red[3][h]));
+        const float mn = __builtin_fmaxf(m_run[r], tmax); // finite: every tile holds a valid token
+        alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - mn);
+        m_run[r] = mn;
+        pv[r] = __builtin_amdgcn_exp2f(sc[r] - mn);
+        l_run[r] = l_run[r] * alpha[r] + pv[r];
+      }
+      put_p(pv);
+      // (skipped when no row maximum of this wave's rows moved: alpha is then 1)
+      if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f) | (alpha[2] != 1.f) | (alpha[3] != 1.f))) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha[r];
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // 4. O[:, 128w + 16ct + j] += P . V over the tile's two 32-token blocks.
     //    B fragment of lane (j, g): V[token 32kb2 + 8g + e][128w + 16ct + j],
     //    e = 0..7, as two LDS transpose reads (ds_read_b64_tr_b16): within a

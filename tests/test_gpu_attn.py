@@ -149,6 +149,27 @@ def test_attn_structured_bit_exact(S, pd):
     assert np.array_equal(gpu[:3], ref["out"][:3])
 
 
+def test_attn_rising_and_falling_scores():
+    """Cached rows scaled page by page by powers of two (x1, x2, x4, x8 in a
+    fixed pattern; exact in bf16, both key and value), so that along each
+    range the scores' running maximum rises by less than 8 (log2 units) on
+    some tiles and by far more on others, and falls back in between: the
+    rescaling of the running sums and outputs is taken mid-range, at several
+    split counts and both partial dtypes."""
+    H = 16
+    inp = make_attn_inputs(8450, H, [4096, 1000, 300])
+    pattern = [0, 1, 0, 2, 0, 0, 3, 1]
+    for m in range(inp.M):
+        for b in range(int(math.ceil(inp.seq_lens[m] / 64))):
+            page = inp.kv[inp.block_table[m, b]]
+            normal = ((page >> 7) & 0xFF) > 0
+            page[normal] += np.uint16(pattern[b % 8] << 7)
+    d = Dev(inp)
+    for S, pd in ((1, BF16P), (4, BF16P), (4, FP32P), (16, BF16P)):
+        gpu, lse, ws = run_attn(d, inp.softmax_scale, S, pd, with_ws=True)
+        assert_attn_parity(gpu, lse, oracle_run(inp, S, pd), inp, S, pd, f"scaled pages S={S} pd={pd}", ws)
+
+
 def test_attn_high_page_indices():
     """A 4.4 GB cache pool (byte offsets past 2^32) with the sequences' pages
     placed at its top end."""
