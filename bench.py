@@ -898,6 +898,7 @@ def cpu_baseline_leg(wl, layers, budget_s):
 
     done_bytes, t_used, n = run(threads, budget_s)
     one_bytes, one_t, one_n = run(1, max(1.0, budget_s / 4))
+    configs = cpu_configs(wl, threads)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -912,7 +913,39 @@ def cpu_baseline_leg(wl, layers, budget_s):
                       f"{t_used:.1f} s with {threads} threads on {cpu} (nproc {os.cpu_count()}); "
                       f"{t_used / n * 1e3:.2f} ms per layer",
             "single_thread": {"value": round(one_bytes / one_t / 1e9, 4), "unit": "GB/s", "cores": 1,
-                              "ms_per_layer": round(one_t / one_n * 1e3, 2), "layer_calls": one_n}}
+                              "ms_per_layer": round(one_t / one_n * 1e3, 2), "layer_calls": one_n},
+            "per_config": configs}
+
+
+def cpu_configs(wl, threads):
+    """The oracle on each shape of the metric's sweep (H = 8, M = 1; H = 16,
+    M = 1..32, BF16 weights; H = 11, M = 1..32; H = 16, MXFP8 weights; BF16
+    output): median of 20 timed calls after 3 untimed ones, with one thread
+    and with `threads` (the oracle threads over heads)."""
+    import oracle
+
+    cases = ([("c0", 8, 0, 1)] + [("c1", 16, 0, m) for m in (1, 2, 4, 8, 16, 32)] +
+             [("c2", 11, 0, m) for m in (1, 3, 7, 16, 32)] + [("c3", 16, 1, m) for m in (1, 8, 32)])
+    rows = []
+    for cfg, h, wf, m in cases:
+        inp = wl.make_inputs(wl.SEED[cfg], H=h, weight_format=wf, M_draw=m)
+        nbytes = wl.algorithmic_bytes(m, h, wf, 0)
+        row = {"config": cfg, "heads": h, "tokens": m, "weights": "bf16" if wf == 0 else "mxfp8",
+               "bytes_per_call": nbytes}
+        for nt, tag in ((1, "one_thread"), (threads, f"threads_{threads}")):
+            ts = []
+            for i in range(23):
+                t0 = time.perf_counter()
+                oracle.mla_query(inp.q_nope, inp.q_pe, inp.w, inp.w_scales, weight_format=wf, out_dtype=0,
+                                 threads=nt, diagnostics=False)
+                if i >= 3:
+                    ts.append(time.perf_counter() - t0)
+            med = float(np.median(ts))
+            row[tag] = {"us_per_call": round(med * 1e6, 1), "gbs": round(nbytes / med / 1e9, 4)}
+        log(f"[bench] cpu oracle {cfg} H={h} M={m} {row['weights']} W: {row['one_thread']['us_per_call']} us (1 thread), "
+            f"{row[f'threads_{threads}']['us_per_call']} us ({threads} threads)")
+        rows.append(row)
+    return rows
 
 
 def _recorded(name, sources, key):
