@@ -6,9 +6,10 @@
 One *step* is a simulated decode step: 64 layers with distinct weight sets
 (32 with BF16 W_UK_T, 32 with MXFP8, alternating), H = 16 heads, M = 32
 tokens, E4M3 output with a per-layer q_scale = amax/448 of the fp32 result,
-the 64 fused calls captured as one hipGraph. Six copies of the 64 weight sets
-(582 MiB) are replayed round-robin, so every layer's weights come from HBM,
-not from the 256 MB Infinity Cache. It runs every step of the path: dispatch,
+the 64 fused calls captured as one hipGraph. Twelve copies of the 64 weight
+sets (1.16 GiB) are replayed round-robin, so every layer's weights come from
+HBM, not from the 256 MB Infinity Cache: the streamed BF16 rows do not
+allocate there, and the MXFP8 layers' 12 copies alone hold 415 MB. It runs every step of the path: dispatch,
 weight streaming, q_nope staging, MXFP8 decode, contraction, rounding, the
 E4M3 epilogue, the q_pe append and the step composition. Per-layer seeds are
 100 * 1004 + layer (see workloads.make_inputs for the recipe). The step's
@@ -64,7 +65,7 @@ HBM_PEAK_GBS = 8000.0
 # Sources whose hash the recorded HBM-traffic figures belong to.
 KERNEL_SOURCES = ("mlaq_kernels.hip", "mlaq_device.h", "mlaq_internal.h")
 ATTN_SOURCES = ("mlaq_attn.hip", "mlaq_device.h", "mlaq_internal.h")
-H, M_STEP, LAYERS, COPIES = 16, 32, 64, 6
+H, M_STEP, LAYERS, COPIES = 16, 32, 64, 12
 
 
 def log(*a):
@@ -407,12 +408,10 @@ def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
         sel = [i for i, L in enumerate(layers) if L.wf == wf]
         res["layers_per_graph"] = len(sel)
         res[wname] = {}
-        # One graph per weight copy. The 32 MXFP8 layers of the step's 6 copies
-        # (207 MB) would fit in the 256 MB Infinity Cache, so MXFP8 gets 6 more
-        # copies of its own (414 MB); BF16's 6 copies hold 402 MB.
+        # One graph per weight copy: the step's 12 copies hold 805 MB of the
+        # BF16 layers and 415 MB of the MXFP8 ones (6 copies of the MXFP8
+        # layers, 207 MB, would fit in the 256 MB Infinity Cache).
         wsets = [[copies[c][i] for i in sel] for c in range(COPIES)]
-        if wf == mq.MLAQ_WEIGHT_MXFP8:
-            wsets += [[layers[i].weights_on_device(torch, mq) for i in sel] for _ in range(COPIES)]
         res["copies"][wname] = len(wsets)
         for od, oname in ((mq.MLAQ_OUT_BF16, "bf16_out"), (mq.MLAQ_OUT_E4M3, "e4m3_out")):
             res[wname][oname] = {}
@@ -455,9 +454,10 @@ def other_heads_cold(torch, mq, wl, args, layers, copies, stream, diag):
     """The smallest case (H = 8, M = 1) and the odd head count (H = 11,
     M = 1/3/7/16/32) per call on cold weights, BF16 weights and output: the
     head slices [0, Hc) and [16 - Hc, 16) of the 32 BF16 layers' weight copies
-    give 12 graphs of 32 calls, replayed round-robin, all copies' first slices
-    before any second slice (384 MiB of distinct weights; at H = 11 the heads
-    both slices share come back after six graphs, 264 MiB of other weights),
+    give 24 graphs of 32 calls, replayed round-robin, all copies' first slices
+    before any second slice (768 MiB of distinct weights at H = 8; at H = 11
+    the heads both slices share come back after twelve graphs, 528 MiB of other
+    weights),
     so every call reads its slab from HBM; streaming hint; each shape beside
     its same-grid floors (empty kernel; pure read of the slab)."""
     bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
@@ -682,7 +682,7 @@ def pages_shape_leg(torch, mq, wl, args):
 
 def uv_leg(torch, mq, wl, args):
     """V up-projection in the same decode-step form: 64 layers (BF16 / MXFP8
-    W_UV alternating), H=16, M=32, one hipGraph per step, 6 rotated weight
+    W_UV alternating), H=16, M=32, one hipGraph per step, 12 rotated weight
     copies (cold), against the staged torch.bmm + copy. Inputs: x ~ N(0,1)
     bf16 [M,H,512]; W_UV ~ N(0, 1/sqrt(512)) as bf16 or E4M3 [H,128,512] with
     E8M0 exponents U{-8..0} along the latent; seeds 100 * 1005 + layer."""
@@ -757,7 +757,7 @@ def uv_leg(torch, mq, wl, args):
     del graphs, sgraphs, staged_w, copies
     torch.cuda.synchronize()
     return {"workload": "V up-projection, 64 layers (BF16/MXFP8 W_UV alternating), H=16, M=32, one hipGraph "
-                        "per step, 6 rotated weight copies (cold)",
+                        "per step, 12 rotated weight copies (cold)",
             "us_per_layer": round(us, 4), "gbs": round(gbs, 1), "us_per_layer_default_hint": round(us_default, 4),
             "staged_us_per_layer": round(s_us, 4), "bytes_per_step": nbytes}
 
@@ -1041,7 +1041,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode step: 64 layers (32 BF16 + 32 MXFP8 W_UK_T, alternating), H=16, M=32, "
-                               "E4M3 out, one hipGraph per step, 6 rotated weight copies (cold HBM)",
+                               "E4M3 out, one hipGraph per step, 12 rotated weight copies (cold HBM)",
                    "heads": H, "tokens": M_STEP, "layers": LAYERS, "nope": 128, "latent": 512, "rope": 64,
                    "bytes_per_step": step["step_bytes"]},
         "us_per_layer": round(ms * 1e3 / LAYERS, 4),

@@ -169,9 +169,10 @@ int mlaq_run(const void* q_nope, const void* q_pe, const void* w, const void* w_
  *       same layer called back to back);
  *   MLAQ_CACHE_STREAM (1): the weights are read once per decode step and are
  *       cold in HBM when the call starts (a model's layers in turn, as in
- *       serving). BF16 weight rows are then loaded, and the output stored,
+ *       serving). BF16 weight rows are then loaded, and a BF16 output stored,
  *       with the nontemporal hint, which shortens a cold call and lengthens a
- *       warm one. MXFP8 weights ignore the hint: their 32-byte row segments
+ *       warm one (an E4M3 output keeps the default store policy, which
+ *       measured faster). MXFP8 weights ignore the hint: their 32-byte row segments
  *       share each 128-byte line among four workgroups, and the hint made
  *       those calls slower.
  * A zero-initialised struct gets MLAQ_CACHE_DEFAULT.

@@ -41,10 +41,13 @@
 //
 // Cache policy. A decode step reads each layer's weights once, cold in HBM;
 // the MLAQ_CACHE_STREAM kernels (template flag NT, BF16 weights only) load
-// the weight rows and store the output with the nontemporal hint, which
+// the weight rows and store a BF16 output with the nontemporal hint, which
 // shortened the cold BF16-weight launch by 8-10% in same-box A/B runs
 // (identical output bits) and lengthened back-to-back calls on one cached
 // weight set by 5-14%, hence a caller's hint rather than the only form.
+// An E4M3 output (32-byte row pieces per workgroup, four workgroups to a
+// 128-byte line) is stored with the default policy: nontemporal, those
+// pieces made the cold M = 32 launch 1.5% longer.
 // A 128-byte line of MXFP8 rows is shared by four workgroups; there every
 // nontemporal form was slower, so those kernels have no NT form.
 //
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   static_assert(PD == 2 || PD == 4, "8- or 16-byte pieces");
   static_assert(WF == MLAQ_WEIGHT_BF16 || NL == 1, "one E4M3 piece (and scale byte) per lane");
   static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 weight rows are streamed nontemporally");
+  constexpr bool kNtOut = NT && OF == MLAQ_OUT_BF16; // nontemporal output stores (BF16 rows only)
   __shared__ __attribute__((aligned(16))) float part[NW * MROWS * LDW];
   __shared__ __attribute__((aligned(16))) uint8_t wtile[NW * 32 * TP];
 
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
     u32x2_t pe_e4 = {0u, 0u};
     if (has_pe) {
       if constexpr (OF == MLAQ_OUT_BF16) {
-        store_out<NT>(at_byte<u32x4_t>(a.out, 2 * pe_o), pe_v);
+        store_out<kNtOut>(at_byte<u32x4_t>(a.out, 2 * pe_o), pe_v);
       } else {
         float x[8];
 #pragma unroll
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
     }
 
     if constexpr (OF == MLAQ_OUT_E4M3) {
-      if (has_pe) store_out<NT>(at_byte<u32x2_t>(a.out, pe_o), pe_e4);
+      if (has_pe) store_out<kNtOut>(at_byte<u32x2_t>(a.out, pe_o), pe_e4);
     }
     // 6. Partial tiles to LDS: lane (j, g) holds tokens 16t + 4g + r of
     //    column 16i + j.
@@ -302,9 +306,9 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
       const uint32_t b01 = bf16x2_rne(sum[0], sum[1]);
       const uint32_t b23 = bf16x2_rne(sum[2], sum[3]);
       if constexpr (OF == MLAQ_OUT_BF16) {
-        store_out<NT>(at_byte<u32x2_t>(a.out, 2 * o), u32x2_t{b01, b23});
+        store_out<kNtOut>(at_byte<u32x2_t>(a.out, 2 * o), u32x2_t{b01, b23});
       } else {
-        store_out<NT>(at_byte<uint32_t>(a.out, o),
+        store_out<kNtOut>(at_byte<uint32_t>(a.out, o),
                       encode(__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u),
                              __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)));
       }
