@@ -11,9 +11,14 @@
 // Decomposition. The call moves ~1-3 MiB of weights and little else, so the
 // kernel is an HBM stream whose cost is latency: every weight byte is
 // requested at kernel entry, spread over as many CUs as the tiling allows.
-// A workgroup of K/32 waves (4 for K = 128, 6 for K = 192) owns one head h
-// and one tile of WC latent columns (WC = 32: 16 workgroups per head), over
-// all K. Wave w takes k rows [32w, 32w+32).
+// A workgroup owns one head h and one tile of WC latent columns (WC = 32:
+// 16 workgroups per head), over all K, in K/(32 KB) waves: wave w takes the
+// KB k-blocks of 32 rows from 32 KB w on. KB = 1 (4 waves at K = 128, 6 at
+// K = 192) for two token tiles; with one token tile fewer, longer waves
+// measured shorter cold launches: KB = 2 at K = 128 (BF16 out -2.7%, MXFP8
+// -0.5..-0.9%, BF16 weights with E4M3 out +0.4%) and KB = 3 at K = 192
+// (the pages' shape, H = 8, M = 1: -7%; M = 4: -6%), while KB = 2 at M = 32
+// lengthened the launch by 1-5% (the epilogue then has fewer threads).
 //
 // Loads. Each lane requests pieces of whole weight rows of up to 16 bytes
 // (the weight is n-major, so a tile's row segment is contiguous): one load
@@ -28,10 +33,11 @@
 // (i + 16g) of A with element e of lane (j + 16g) of B, for output (i, j):
 // A is q_nope of token i over 8 consecutive k (one 16-byte load straight
 // from global memory), B is the weight column j over the same 8 k. A wave
-// writes its 32 x WC bf16 tile (MXFP8 decoded first) to its own LDS slice
+// writes its 32 KB x WC bf16 tile (MXFP8 decoded first) to its own LDS slice
 // and reads the B fragments back with the gfx950 transpose read, so no
-// workgroup barrier separates the loads from the MFMAs. M <= 16 uses one
-// 16-token tile, M <= 32 two.
+// workgroup barrier separates the loads from the MFMAs; its KB k-blocks are
+// chained in ascending k in one accumulator. M <= 16 uses one 16-token
+// tile, M <= 32 two.
 //
 // The waves' fp32 partial tiles are summed through LDS in a fixed order
 // (wave 0 + 1 + 2 + ...), so results are deterministic. The epilogue rounds to
@@ -80,26 +86,26 @@ struct Flag {
 
 // ---------------------------------------------------------------------------
 // The fused kernel. One workgroup per head and WC-column tile (WC = 32 or
-// 16; wave w owns k rows [32w, 32w+32)); each lane loads whole pieces of
-// weight rows, of up to 16 bytes: the
-// wave's 32 x WC tile is RBY = WC * (bytes per weight) bytes per row, every
-// lane takes RBY/2 of them (16 or 32 bytes for BF16, 8 or 16 for E4M3) in
-// loads of PB bytes, LPR lanes per row segment, so each load instruction
-// covers 64/LPR whole row segments. MXFP8 rows come with the one scale byte
+// 16; wave w owns k rows [32 KB w, 32 KB (w+1))); each lane loads whole
+// pieces of weight rows, of up to 16 bytes: a row segment of the wave's tile
+// is RBY = WC * (bytes per weight) bytes, every lane takes RBY/2 of them per
+// 32 rows (16 or 32 bytes for BF16, 8 or 16 for E4M3) in loads of PB bytes,
+// LPR lanes per row segment, so each load instruction covers 64/LPR whole row
+// segments. MXFP8 rows come with the one scale byte
 // of that row and column group, and are decoded to bf16 in registers. The
 // wave then writes its 32 x WC bf16 tile to its own LDS slice and reads the
 // MFMA B fragments back with the gfx950 transpose read (ds_read_b64_tr_b16):
 // within a 16-lane group, output lane i gets element i%4 of the 8 bytes that
 // lane 4e + i/4 points at, so lane 4e + q points at columns 4q..4q+3 of k row
 // 8g + e (and 8g + 4 + e for the second read), and lane (j, g) receives k rows
-// 8g..8g+7 of column j: exactly the B operand pairing with the q_nope A
-// fragment of the same k. Each wave reads only rows it wrote itself, so the
+// 8g..8g+7 of column j (of each k-block): exactly the B operand pairing with
+// the q_nope A fragment of the same k. Each wave reads only rows it wrote itself, so the
 // hand-off needs no workgroup barrier. Every output sums the same products in
 // the same MFMA positions whatever WC is, so the tile widths give identical
 // bits.
 // ---------------------------------------------------------------------------
 
-template <int WF, int OF, int MT, int NW, bool NT, int WC>
+template <int WF, int OF, int MT, int NW, bool NT, int WC, int KB>
 __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
     const uint16_t* q_pe, const void* w, const uint16_t* q_nope, const uint8_t* w_scales, const float* q_scale,
     uint32_t pe_sm, uint32_t q_sm, uint32_t head_strides, uint32_t m_h, void* out, uint32_t out_sm, uint32_t out_sh) {
@@ -112,7 +118,8 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   // bits) and q_pe (high), m_h packs M (low 16 bits) and H (high).
   const FusedArgs a{q_nope, q_pe, w, w_scales, q_scale, out, q_sm, head_strides & 0xffffu, pe_sm,
                     head_strides >> 16, out_sm, out_sh, int(m_h & 0xffffu), int(m_h >> 16)};
-  constexpr int K = 32 * NW;
+  constexpr int K = 32 * NW * KB;
+  constexpr int KR = 32 * KB;                           // k rows per wave
   constexpr int THREADS = 64 * NW;
   constexpr int NCT = kLatent / WC;
   constexpr int MROWS = 16 * MT;
@@ -121,18 +128,17 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   constexpr int ESZ = (WF == MLAQ_WEIGHT_BF16) ? 2 : 1; // bytes per weight in HBM
   constexpr int RBY = WC * ESZ;                         // bytes per row segment
   constexpr int PB = RBY / 2 < 16 ? RBY / 2 : 16;       // bytes per load
-  constexpr int NL = (RBY / 2) / PB;                    // loads per lane
+  constexpr int NL = KB * ((RBY / 2) / PB);             // loads per lane
   constexpr int LPR = RBY / PB;                         // lanes per row segment
   constexpr int RPL = 64 / LPR;                         // row segments per load
   constexpr int PD = PB / 4;                            // dwords per load
   constexpr int OD = PD * (2 / ESZ);                    // bf16 dwords per load
   static_assert(WC == 16 || WC == 32, "tiles of 16 or 32 columns");
   static_assert(PD == 2 || PD == 4, "8- or 16-byte pieces");
-  static_assert(WF == MLAQ_WEIGHT_BF16 || NL == 1, "one E4M3 piece (and scale byte) per lane");
   static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 weight rows are streamed nontemporally");
   constexpr bool kNtOut = NT && OF == MLAQ_OUT_BF16; // nontemporal output stores (BF16 rows only)
   __shared__ __attribute__((aligned(16))) float part[NW * MROWS * LDW];
-  __shared__ __attribute__((aligned(16))) uint8_t wtile[NW * 32 * TP];
+  __shared__ __attribute__((aligned(16))) uint8_t wtile[NW * KR * TP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   const int h = tile / NCT, ct = tile - h * NCT;
   const int c0 = ct * WC;
   const int M = a.M;
-  const int k0 = 32 * wave + 8 * g;      // first k of this lane's A and B fragments
+  const int k0 = KR * wave + 8 * g;      // first k of this lane's A and B fragments (k-block 0)
   const int r0 = lane / LPR;             // wave-local row of this lane's first piece (+RPL per load)
   const int pcol = (PB / ESZ) * (lane % LPR); // first tile column of each piece
 
@@ -158,9 +164,9 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
 
   // 2. This lane's pieces of its weight rows (and scale byte).
   uint32_t wv[NL][PD];
-  uint32_t sb = 0;
+  uint32_t sb[NL];                       // MXFP8: the scale byte of each piece's row
   {
-    const uint32_t off = ((uint32_t(h) * K + 32 * wave + r0) * kLatent + c0 + pcol) * ESZ; // < 2^22
+    const uint32_t off = ((uint32_t(h) * K + KR * wave + r0) * kLatent + c0 + pcol) * ESZ; // < 2^22
     __builtin_assume(off < (1u << 22));
 #pragma unroll
     for (int v = 0; v < NL; ++v) {
@@ -178,18 +184,22 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
       }
     }
     if constexpr (WF == MLAQ_WEIGHT_MXFP8)
-      sb = a.w_scales[(uint32_t(h) * K + 32 * wave + r0) * kScalesPerRow + (c0 / kMxBlock)];
+#pragma unroll
+      for (int v = 0; v < NL; ++v)
+        sb[v] = a.w_scales[(uint32_t(h) * K + KR * wave + r0 + RPL * v) * kScalesPerRow + (c0 / kMxBlock)];
   }
 
   // 3. q_nope A fragments: token 16t + j, k rows k0..k0+7. Rows past M read
   //    token 0 instead; MFMA output row i depends only on A row i, and rows
   //    past M are never stored, so they need no zeroing.
-  u32x4_t qa[MT];
+  u32x4_t qa[MT][KB];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + j;
     const int mc = m < M ? m : 0;
-    qa[t] = *at_byte<const u32x4_t>(a.q_nope, 2 * (__umul24(mc, a.q_sm) + __umul24(h, a.q_sh) + k0));
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qa[t][kb] = *at_byte<const u32x4_t>(a.q_nope, 2 * (__umul24(mc, a.q_sm) + __umul24(h, a.q_sh) + k0 + 32 * kb));
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
 
     // 5. The weight pieces as bf16 (exact decode for MXFP8) into this wave's
     //    LDS tile, then the B fragments back through the transpose read.
-    uint8_t* wt = wtile + wave * 32 * TP;
+    uint8_t* wt = wtile + wave * KR * TP;
 #pragma unroll
     for (int v = 0; v < NL; ++v) {
       uint32_t b[OD];
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
 #pragma unroll
         for (int d = 0; d < PD; ++d) b[d] = wv[v][d];
       } else {
-        const float sc = e8m0_scale_operand(sb);
+        const float sc = e8m0_scale_operand(sb[v]);
 #pragma unroll
         for (int d = 0; d < PD; ++d) {
           b[2 * d] = e4m3x2_scaled_bf16(wv[v][d], sc, false);
@@ -262,8 +272,9 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int i = 0; i < WC / 16; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* src = wt + (8 * g + (j >> 2)) * TP + 8 * (j & 3);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint8_t* src = wt + (32 * kb + 8 * g + (j >> 2)) * TP + 8 * (j & 3);
 #pragma unroll
       for (int i = 0; i < WC / 16; ++i) {
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(src + 32 * i));
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
 #pragma unroll
         for (int t = 0; t < MT; ++t)
           acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, qa[t]), __builtin_bit_cast(bf16x8_t, bf), acc[t][i], 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, qa[t][kb]), __builtin_bit_cast(bf16x8_t, bf), acc[t][i], 0, 0, 0);
       }
     }
 
@@ -324,11 +335,14 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   }
 }
 
-template <int WF, int OF, int MT, int NW, bool NT = false>
+template <int WF, int OF, int MT, int NW, bool NT, int KB>
 const void* kernel_ptr(int wc) {
-  if (wc == 16) return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 16>);
-  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 32>);
+  if (wc == 16) return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 16, KB>);
+  return reinterpret_cast<const void*>(&fused_query_kernel<WF, OF, MT, NW, NT, 32, KB>);
 }
+
+// k-blocks of 32 rows per wave (the header above gives the measurements).
+constexpr int k_blocks_per_wave(int K, int MT) { return MT == 1 ? (K == 192 ? 3 : 2) : 1; }
 
 } // namespace
 
@@ -336,10 +350,11 @@ const void* kernel_for(const Variant& v) {
   if (v.cols != 16 && v.cols != 32) return nullptr;
 #define MLAQ_CASE(WF, OF, MT, K)                                                                 \
   if (v.weight_format == WF && v.out_dtype == OF && v.m_tiles == MT && v.nope == K) {      \
+    constexpr int KB = k_blocks_per_wave(K, MT), NW = K / (32 * KB);                       \
     if constexpr (WF == MLAQ_WEIGHT_BF16)                                                  \
-      return v.stream ? kernel_ptr<WF, OF, MT, K / 32, true>(v.cols) : kernel_ptr<WF, OF, MT, K / 32>(v.cols); \
+      return v.stream ? kernel_ptr<WF, OF, MT, NW, true, KB>(v.cols) : kernel_ptr<WF, OF, MT, NW, false, KB>(v.cols); \
     else                                                                                   \
-      return v.stream ? nullptr : kernel_ptr<WF, OF, MT, K / 32>(v.cols);                  \
+      return v.stream ? nullptr : kernel_ptr<WF, OF, MT, NW, false, KB>(v.cols);           \
   }
 #define MLAQ_CASES(K)                                \
   MLAQ_CASE(MLAQ_WEIGHT_BF16, MLAQ_OUT_BF16, 1, K)  \
@@ -360,7 +375,7 @@ const void* kernel_for(const Variant& v) {
 void launch_shape(const Variant& v, int H, dim3* grid, dim3* block) {
   // One workgroup per head and column tile of the kernel kernel_for() picks.
   *grid = dim3(unsigned(H * (kLatent / v.cols)), 1, 1);
-  *block = dim3(unsigned(64 * (v.nope / 32)), 1, 1);
+  *block = dim3(unsigned(64 * (v.nope / (32 * k_blocks_per_wave(v.nope, v.m_tiles)))), 1, 1);
 }
 
 } // namespace mlaq
