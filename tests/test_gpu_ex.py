@@ -73,10 +73,12 @@ def test_k192_e4m3_out(wf, H, M):
     assert_e4m3_parity(run_contiguous(inp, E4M3, qs), run_oracle(inp, E4M3, qs), f"K=192 e4m3 wf={wf} H={H} M={M}")
 
 
-def test_k192_structured_bit_exact():
+@pytest.mark.parametrize("M", [9, 32])
+def test_k192_structured_bit_exact(M):
     """Identity weights (W[h,k,n] = 1 iff n = k + 64 (h mod 5)) and the all-ones
-    MXFP8 payload with E8M0 bytes 127 - ((h+k+j) mod 9): exact in any order."""
-    H, M, K = 16, 32, 192
+    MXFP8 payload with E8M0 bytes 127 - ((h+k+j) mod 9): exact in any order
+    (M = 9: one token tile, whose waves hold three k-blocks each)."""
+    H, K = 16, 192
     rng = np.random.Generator(np.random.PCG64(901))
     q = bf16_bits(rng.standard_normal((M, H, K), dtype=np.float32))
     pe = bf16_bits(rng.standard_normal((M, H, 64), dtype=np.float32))
