@@ -24,7 +24,8 @@
 // (the weight is n-major, so a tile's row segment is contiguous): one load
 // instruction covers 16 (BF16) or 32 (E4M3) whole row segments, and an MXFP8
 // lane also loads the one E8M0 byte of its row and column group, 5 memory
-// requests per wave in all with q_pe and the q_nope fragments. The
+// requests per wave of one k-block in all with q_pe and the q_nope
+// fragments (a k-block more adds its weight piece(s) and fragment). The
 // arguments the first requests need are the kernel's first scalar
 // arguments, which arrive preloaded in SGPRs (no kernel-argument load on the
 // critical path).
@@ -93,7 +94,7 @@ struct Flag {
 // LPR lanes per row segment, so each load instruction covers 64/LPR whole row
 // segments. MXFP8 rows come with the one scale byte
 // of that row and column group, and are decoded to bf16 in registers. The
-// wave then writes its 32 x WC bf16 tile to its own LDS slice and reads the
+// wave then writes its 32 KB x WC bf16 tile to its own LDS slice and reads the
 // MFMA B fragments back with the gfx950 transpose read (ds_read_b64_tr_b16):
 // within a 16-lane group, output lane i gets element i%4 of the 8 bytes that
 // lane 4e + i/4 points at, so lane 4e + q points at columns 4q..4q+3 of k row
