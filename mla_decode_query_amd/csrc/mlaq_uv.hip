@@ -13,29 +13,31 @@
 // directly its B fragment for v_mfma_f32_16x16x32_bf16, and the A fragment
 // is the same 8 c of token j's x row. The MFMA sums element e of lane
 // j + 16g of A against element e of lane i + 16g of B over all g and e, so
-// any assignment of c to (g, e) that A and B share is valid. BF16 weights:
-// lane (j, g) of wave w takes c = 128w + 32kb + 8g + e in k-block kb, so one
-// load instruction covers 64 contiguous bytes of each of 16 rows. MXFP8
-// weights: the lane takes the 32 consecutive c in [128w + 32g, +32), one MX
-// scale group, 8 per k-block (c = 128w + 32g + 8kb + e): two 16-byte loads
-// and one scale byte per lane instead of four 8-byte loads and their scale
-// bytes. (The grouped form made cold BF16 launches with nontemporal loads
-// about 10% longer: each instruction then touches every 128-byte line of a
-// row segment in 16-byte pieces.) A workgroup (4 waves) owns one head, CB value columns and
-// one 16-token tile; wave w reduces c in [128w, 128w+128) over four MFMAs,
-// and the four partial tiles are summed through LDS in a fixed order. Every workgroup reads its head's x rows for its tile from L2, which
-// is the per-CU traffic that grows with M, so the shape keeps 256 workgroups
-// at H = 16 either way: for M <= 16, CB = 8 (the upper 8 MFMA columns repeat
-// the lower 8 at the same addresses, so no extra HBM traffic, and are
-// dropped), 16 workgroups per head; for M <= 32, CB = 16 and the two token
-// tiles in workgroups of their own (8 column blocks x 2 tiles per head), the
-// two tiles of a column block on the same XCD so its weights come from HBM
-// once.
+// any assignment of c to (g, e) that A and B share is valid. A workgroup of
+// W waves (W = 1 here; each wave reduces S = 512/W latent values in S/32
+// k-blocks, chained in one accumulator) owns one head, CB value columns and
+// one 16-token tile. BF16 weights: lane (j, g) of wave w takes
+// c = S w + 32kb + 8g + e in k-block kb, so one load instruction covers 64
+// contiguous bytes of each of 16 rows. MXFP8 weights: the lane takes
+// S/4 consecutive c from S w + (S/4) g (c = S w + (S/4) g + 8kb + e), i.e.
+// whole MX scale groups of 32 (four with one wave), in 16-byte loads and one
+// scale byte per group, instead of 8-byte loads and a scale byte for each.
+// (The grouped form made cold BF16 launches with nontemporal loads about 10%
+// longer: each instruction then touches every 128-byte line of a row segment
+// in 16-byte pieces.) The waves' partial tiles are summed through LDS in a
+// fixed order, and the tile goes through LDS anyway so that each thread
+// stores 4 consecutive columns. Every workgroup reads its head's x rows for
+// its tile from L2, which is the per-CU traffic that grows with M, so the
+// shape keeps 256 workgroups at H = 16 either way: for M <= 16, CB = 8 (the
+// upper 8 MFMA columns repeat the lower 8 at the same addresses, so no extra
+// HBM traffic, and are dropped), 16 workgroups per head; for M <= 32, CB = 16
+// and the two token tiles in workgroups of their own (8 column blocks x 2
+// tiles per head), the two tiles of a column block on the same XCD so its
+// weights come from HBM once.
 //
-// MXFP8: a lane loads its 32 E4M3 bytes (two 16-byte loads) and the one
-// E8M0 byte of their group; v_cvt_scalef32_pk_bf16_fp8 gives the exact bf16
-// of each byte times 2^(S-127), so the MFMA forms exact products as the
-// oracle's dequantization does.
+// MXFP8: v_cvt_scalef32_pk_bf16_fp8 gives the exact bf16 of each E4M3 byte
+// times 2^(S-127), so the MFMA forms exact products as the oracle's
+// dequantization does.
 #include "mlaq.h"
 #include "mlaq_device.h"
 #include "mlaq_internal.h"
@@ -45,7 +47,16 @@ namespace {
 
 using namespace dev;
 
-constexpr int kUvThreads = 256; // 4 waves
+// Waves per workgroup, each reducing kUvSpan latent values in kUvKb
+// k-blocks of 32. One wave over all 512 measured shortest in same-box A/B
+// runs over cold rotations (against four waves of 128: -2.1% BF16, -2.8%
+// MXFP8 at M = 32, -2.9% both at M = 8; two waves of 256 were in between,
+// eight waves of 64 were 2-6% slower).
+constexpr int kUvWaves = 1;
+constexpr int kUvThreads = 64 * kUvWaves;
+constexpr int kUvKb = 16 / kUvWaves;    // k-blocks of 32 latent values per wave
+constexpr int kUvSpan = 512 / kUvWaves; // latent values per wave
+static_assert(kUvWaves == 1 || kUvWaves == 2 || kUvWaves == 4 || kUvWaves == 8, "k-blocks split evenly");
 constexpr int kUvScalesPerRow = kLatent / kMxBlock;
 
 // NT (MLAQ_CACHE_STREAM, BF16 weights only): the W_UV rows are loaded with
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   constexpr int LDW = CB + 4;
   static_assert(CB == 8 || CB == 16, "8 or 16 value columns per workgroup");
   static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 W_UV rows are streamed nontemporally");
-  __shared__ __attribute__((aligned(16))) float part[4 * MROWS * LDW];
+  __shared__ __attribute__((aligned(16))) float part[kUvWaves * MROWS * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -79,15 +90,16 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   // This lane's first latent value, and the step between its k-blocks.
   constexpr bool kGrouped = WF == MLAQ_WEIGHT_MXFP8;
   constexpr int kStep = kGrouped ? 8 : 32;
-  const int cbase = 128 * wave + (kGrouped ? 32 : 8) * g;
+  const int cbase = kUvSpan * wave + (kGrouped ? 8 * kUvKb : 8) * g;
 
-  // 1. Weight fragments: 4 k-blocks of 8 consecutive latent values.
-  u32x4_t wb[4];
-  uint32_t sc = 0;
+  // 1. Weight fragments: kUvKb k-blocks of 8 consecutive latent values.
+  u32x4_t wb[kUvKb];
+  constexpr int kGroups = kUvKb >= 4 ? kUvKb / 4 : 1; // MX scale groups a lane's latent values touch
+  uint32_t sc[kGroups];
   if constexpr (WF == MLAQ_WEIGHT_BF16) {
     const uint32_t off = ((uint32_t(h) * kValue + v) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kUvKb; ++kb) {
       if constexpr (NT)
         wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb));
       else
@@ -95,36 +107,38 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
     }
   } else {
     const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
-    const u32x4_t w0 = *at_byte<const u32x4_t>(a.w, off);
-    const u32x4_t w1 = *at_byte<const u32x4_t>(a.w, off + 16);
-    sc = a.w_scales[(uint32_t(h) * kValue + v) * kUvScalesPerRow + cbase / kMxBlock];
-    wb[0] = u32x4_t{w0[0], w0[1], 0u, 0u}; // decoded below
-    wb[1] = u32x4_t{w0[2], w0[3], 0u, 0u};
-    wb[2] = u32x4_t{w1[0], w1[1], 0u, 0u};
-    wb[3] = u32x4_t{w1[2], w1[3], 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q)
+      sc[q] = a.w_scales[(uint32_t(h) * kValue + v) * kUvScalesPerRow + cbase / kMxBlock + q];
+#pragma unroll
+    for (int q = 0; q < kUvKb / 2; ++q) {
+      const u32x4_t wq = *at_byte<const u32x4_t>(a.w, off + 16 * q);
+      wb[2 * q] = u32x4_t{wq[0], wq[1], 0u, 0u}; // decoded below
+      wb[2 * q + 1] = u32x4_t{wq[2], wq[3], 0u, 0u};
+    }
   }
 
   // 2. A fragments: token 16 mt + j, the same 8 latent values per k-block.
   //    Rows past M read token 0; their MFMA output rows are never stored.
-  u32x4_t xa[4];
+  u32x4_t xa[kUvKb];
   {
     const int m = 16 * mt + j;
     const int mc = m < M ? m : 0;
     const uint32_t off = ((uint32_t(mc) * H + h) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 2 * kStep * kb);
+    for (int kb = 0; kb < kUvKb; ++kb) xa[kb] = *at_byte<const u32x4_t>(a.x, off + 2 * kStep * kb);
   }
   __builtin_amdgcn_sched_barrier(0); // every load is in flight before any wait
 
-  // 3. Contraction over this wave's 128 latent values.
+  // 3. Contraction over this wave's kUvSpan latent values.
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < kUvKb; ++kb) {
     u32x4_t b = wb[kb];
     if constexpr (WF == MLAQ_WEIGHT_MXFP8) {
       // 8 E4M3 values of one column (consecutive latent) -> 4 dwords of bf16
       // pairs, one scaled conversion each.
-      const float s = e8m0_scale_operand(sc);
+      const float s = e8m0_scale_operand(sc[kUvKb >= 4 ? kb / 4 : 0]); // a lane's groups start at a group boundary
       u32x4_t d;
 #pragma unroll
       for (int p = 0; p < 4; ++p) d[p] = e4m3x2_scaled_bf16(b[p >> 1], s, p & 1);
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   }
   __syncthreads();
 
-  // 5. Epilogue: sum the four partials in order, round, store 4 columns.
+  // 5. Epilogue: sum the waves' partials in order, round, store 4 columns.
   constexpr int GPR = CB / 4;
   const int m0 = 16 * mt, rows = M - m0 < MROWS ? M - m0 : MROWS; // tokens of this tile below M
   for (int x = tid; x < rows * GPR; x += kUvThreads) {
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
     const int off = ml * LDW + 4 * cg;
     f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + off);
 #pragma unroll
-    for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
+    for (int w = 1; w < kUvWaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(part + w * MROWS * LDW + off);
     const uint32_t o = (uint32_t(m) * H + h) * kValue + vb * CB + 4 * cg;
     *at_byte<u32x2_t>(a.out, 2 * o) = u32x2_t{bf16x2_rne(sum[0], sum[1]), bf16x2_rne(sum[2], sum[3])};
   }
