@@ -350,41 +350,47 @@ def shape_floors(torch, diag, grid, weight_sets, stream, steps, warmup):
             "read_bytes": nbytes}
 
 
+def read_store_floor(torch, diag, weight_sets, rows, row_bytes, store_bytes, stream, steps, warmup):
+    """Per-node time of a pure read of each layer's weight payload by
+    H x 16 workgroups (as in shape_floors) followed, once the loads arrive,
+    by `rows` output rows of `row_bytes` stored in the fused kernel's epilogue
+    pattern (8 threads per row and 32-column tile, `store_bytes` each: 4 for
+    E4M3, 8 for BF16 output), into buffers of its own; no arithmetic, no
+    q_pe columns, plain loads and stores. weight_sets as in shape_floors."""
+    n = len(weight_sets[0])
+    outs = [torch.empty((rows, H, row_bytes), dtype=torch.uint8, device="cuda") for _ in range(n)]
+
+    def body(ws):
+        st = torch.cuda.current_stream().cuda_stream
+        for (w, _), o in zip(ws, outs):
+            assert diag.mlaqdiag_read_store_grid(w.data_ptr(), w.numel() * w.element_size(), o.data_ptr(), o.numel(),
+                                                 rows, H * row_bytes, row_bytes, 16, store_bytes, H * 16, st) == 0
+
+    graphs = []
+    for ws in weight_sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                body(ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return time_graphs(torch, graphs, steps, warmup, per_step_units=n) * 1e3
+
+
 def floors_leg(torch, mq, layers, copies, stream, args):
     """Per-node floors of the dominant kernel's launch shape (256 workgroups)
     in the same graph loop: an empty kernel and a pure read of each BF16
-    layer's 2 MiB weight slab with the same cold rotation."""
+    layer's 2 MiB weight slab with the same cold rotation, and that read
+    followed by the dominant kernel's E4M3 output rows ([32,16,576], 32 bytes
+    per row and tile) stored in its epilogue's pattern."""
     diag = diag_lib()
     if diag is None:
         return None
     bf = [i for i, L in enumerate(layers) if L.wf == mq.MLAQ_WEIGHT_BF16]
-    f = shape_floors(torch, diag, 256, [[copies[c][i] for i in bf] for c in range(COPIES)], stream, args.steps,
-                     args.warmup)
+    wsets = [[copies[c][i] for i in bf] for c in range(COPIES)]
+    f = shape_floors(torch, diag, 256, wsets, stream, args.steps, args.warmup)
     log(f"[bench] floors: empty kernel {f['empty_kernel_us']:.3f} us/node, cold 2 MiB read {f['cold_read_us']:.3f} us/node")
-    # Read and store: the same reads, then the dominant kernel's E4M3 output
-    # rows ([32,16,576], 32 bytes per row and tile, 8 threads per row) stored
-    # in its epilogue's pattern once the loads arrive, into buffers of its own.
-    outs = [torch.empty((M_STEP, H, mq.ROW), dtype=torch.uint8, device="cuda") for _ in bf]
-
-    def rs_body_for(c):
-        def body():
-            st = torch.cuda.current_stream().cuda_stream
-            for i, o in zip(bf, outs):
-                w, _ = copies[c][i]
-                assert diag.mlaqdiag_read_store_grid(w.data_ptr(), w.numel() * w.element_size(), o.data_ptr(),
-                                                     o.numel(), M_STEP, H * mq.ROW, mq.ROW, mq.LATENT_DIM // 32, 4,
-                                                     256, st) == 0
-        return body
-
-    graphs = []
-    for c in range(COPIES):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
-                rs_body_for(c)()
-        graphs.append(g)
-    torch.cuda.synchronize()
-    rs_us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=len(bf)) * 1e3
+    rs_us = read_store_floor(torch, diag, wsets, M_STEP, mq.ROW, 4, stream, args.steps, args.warmup)
     log(f"[bench] floors: cold 2 MiB read + the E4M3 output stores {rs_us:.3f} us/node")
     return {"empty_kernel_us": f["empty_kernel_us"], "cold_read_2MiB_us": f["cold_read_us"],
             "cold_read_store_us": round(rs_us, 4),
@@ -443,9 +449,17 @@ def per_call_cold_leg(torch, mq, wl, args, layers, copies, stream):
                 del graphs
         if diag is not None:
             f = shape_floors(torch, diag, H * 16, wsets, stream, args.steps, args.warmup)
+            # The same read followed by the output rows' stores, at both ends
+            # of the M sweep.
+            f["cold_read_store_us"] = {}
+            for oname, row_bytes, sb in (("bf16_out", 2 * mq.ROW, 8), ("e4m3_out", mq.ROW, 4)):
+                f["cold_read_store_us"][oname] = {
+                    str(M): round(read_store_floor(torch, diag, wsets, M, row_bytes, sb, stream, args.steps,
+                                                   args.warmup), 4) for M in (1, 32)}
             res["floors"][wname] = f
             log(f"[bench] per-call cold {wname} W floors ({f['grid']} workgroups): empty kernel "
-                f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us")
+                f"{f['empty_kernel_us']:.3f} us, pure read of {f['read_bytes']} B {f['cold_read_us']:.3f} us, "
+                f"read + output stores {f['cold_read_store_us']}")
     res["heads"] = other_heads_cold(torch, mq, wl, args, layers, copies, stream, diag)
     return res
 
