@@ -1,4 +1,7 @@
-"""Seeded sweep over the fused query's launch space through mlaq_run_ex: each
+"""Seeded sweeps over the launch spaces of the fused query and of the dense
+MLA decode attention.
+
+Fused query, through mlaq_run_ex: each
 case draws a head count (8, 11, 16), a token count (1..32), the nope width
 (128 or 192), the weight format, the output type, the cache hint and strided
 layouts for q_nope, q_pe and the output (token- or head-major storage with
@@ -6,20 +9,31 @@ padded rows and heads, sparkinfer PR #75 "[GG] Add BF16 MLA query projection
 and assembly", "What" and "Validation": the [H,M,K] batch view and pitched
 outputs), and checks the result against the oracle on contiguous copies.
 Padding around the output rows must stay untouched. Same parity bar as
-tests/test_gpu_parity.py."""
+tests/test_gpu_parity.py.
+
+Attention, through mlaq_attn_run (b12x PR #441 "Allow FP32 split partials in
+prepared dense MLA": BF16 or FP32 partials, validation against a reference of
+higher precision): each case draws the head count (1..16), the page size,
+the batch, sequence lengths that mix empty, single-token, page-edge and long
+sequences, the split count and the partial dtype, and checks the output, the
+lse and the partials read back from the workspace against the oracle's split
+procedure with the same split count and partial dtype (the bar of
+tests/test_gpu_attn.py)."""
 
 import numpy as np
 import pytest
 import torch
 
 import mla_decode_query_amd as mq
-from gpu_util import assert_bf16_parity, assert_e4m3_parity, dev_bf16, dev_u8, out_bits, run_oracle
-from workloads import WEIGHT_BF16, WEIGHT_MXFP8, make_inputs
+from gpu_util import (BF16P, FP32P, assert_attn_parity, assert_bf16_parity, assert_e4m3_parity, attn_oracle_run,
+                      dev_bf16, dev_u8, out_bits, run_oracle)
+from workloads import WEIGHT_BF16, WEIGHT_MXFP8, make_attn_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 
 BF16, E4M3 = mq.MLAQ_OUT_BF16, mq.MLAQ_OUT_E4M3
 CASES = 40
+ATTN_CASES = 24
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -95,3 +109,37 @@ def test_random_launch(i):
     if c["out_pad"]:
         pad = out_bits(ws[..., mq.ROW:].contiguous())
         assert np.all(pad == canary), f"{what}: output padding was written"
+
+
+def draw_attn(i):
+    """The i-th attention case (a fixed function of i)."""
+    rng = np.random.default_rng(880_000 + i)
+    P = int(rng.choice([1, 8, 16, 48, 64, 128, 256]))
+    M = int(rng.integers(1, 6))
+    lens = []
+    for _ in range(M):
+        kind = rng.integers(0, 6)
+        lens.append(int([0, 1, max(P - 1, 1), P, P + 1, int(rng.integers(2, 3000))][kind]))
+    return dict(H=int(rng.integers(1, 17)), P=P, lens=lens, S=int(rng.choice([1, 2, 3, 5, 8, 16, 33])),
+                pd=int(rng.choice([BF16P, FP32P])), seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("i", range(ATTN_CASES))
+def test_random_attention(i):
+    c = draw_attn(i)
+    what = f"attention case {i}: {c}"
+    print(what, flush=True)
+    inp = make_attn_inputs(c["seed"], c["H"], c["lens"], page_size=c["P"])
+    M, H, S, pd = inp.q.shape[0], c["H"], c["S"], c["pd"]
+    q = dev_bf16(inp.q)
+    kv = dev_bf16(inp.kv)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    out = torch.empty((M, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    n = mq.mlaq_attn_workspace_size(M, H, S, pd)
+    ws = torch.empty((n,), dtype=torch.uint8, device="cuda") if n else None
+    mq.mlaq_attn_run(q, kv, bt, sl, out, inp.softmax_scale, S, pd, ws, lse)
+    torch.cuda.synchronize()
+    gpu, gpu_lse = out_bits(out), lse.cpu().numpy().astype(np.float64)
+    assert_attn_parity(gpu, gpu_lse, attn_oracle_run(inp, S, pd), inp, S, pd, what, ws)
