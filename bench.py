@@ -720,24 +720,17 @@ def uv_leg(torch, mq, wl, args):
     for wf in (mq.MLAQ_WEIGHT_BF16, mq.MLAQ_WEIGHT_MXFP8):
         mq.mlaq_uv_prewarm(Hh, [M], wf)
     torch.cuda.synchronize()
-    def uv_graphs(hint):
-        gs = []
-        for c in range(C):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
-                with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
-                    for d, (w, sc) in zip(lay, copies[c]):
-                        mq.mlaq_uv_run_ex(d["x"], w, sc, d["out"], d["wf"], cache_hint=hint)
-            gs.append(g)
-        torch.cuda.synchronize()
-        return gs
-
-    # W_UV is read once per step (cold): the streaming hint; the default hint beside it.
-    graphs = uv_graphs(mq.MLAQ_CACHE_STREAM)
+    # W_UV is read once per step (cold); the UV kernels take no cache hint.
+    graphs = []
+    for c in range(C):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream, capture_error_mode="global"):
+                for d, (w, sc) in zip(lay, copies[c]):
+                    mq.mlaq_uv_run(d["x"], w, sc, d["out"], d["wf"])
+        graphs.append(g)
+    torch.cuda.synchronize()
     us = time_graphs(torch, graphs, args.steps, args.warmup, per_step_units=L) * 1e3
-    dgraphs = uv_graphs(mq.MLAQ_CACHE_DEFAULT)
-    us_default = time_graphs(torch, dgraphs, args.steps, args.warmup, per_step_units=L) * 1e3
-    del dgraphs
     nbytes = sum(128 * 512 * Hh * (2 if d["wf"] == 0 else 1) + (0 if d["s"] is None else Hh * 128 * 16)
                  + M * Hh * 512 * 2 + M * Hh * 128 * 2 for d in lay)
     # staged: materialized bf16 W_UV^T [H,512,128] (contiguous) + bmm + copy
@@ -766,14 +759,14 @@ def uv_leg(torch, mq, wl, args):
     torch.cuda.synchronize()
     s_us = time_graphs(torch, sgraphs, args.steps, args.warmup, per_step_units=L) * 1e3
     gbs = nbytes / L / (us * 1e-6) / 1e9
-    log(f"[bench] UV projection (H=16, M=32, 64 cold layers): fused {us:.3f} us/layer ({gbs:.1f} GB/s, streaming "
-        f"hint; default hint {us_default:.3f}), staged {s_us:.3f} us/layer")
+    log(f"[bench] UV projection (H=16, M=32, 64 cold layers): fused {us:.3f} us/layer ({gbs:.1f} GB/s), "
+        f"staged {s_us:.3f} us/layer")
     del graphs, sgraphs, staged_w, copies
     torch.cuda.synchronize()
     return {"workload": "V up-projection, 64 layers (BF16/MXFP8 W_UV alternating), H=16, M=32, one hipGraph "
                         "per step, 12 rotated weight copies (cold)",
-            "us_per_layer": round(us, 4), "gbs": round(gbs, 1), "us_per_layer_default_hint": round(us_default, 4),
-            "staged_us_per_layer": round(s_us, 4), "bytes_per_step": nbytes}
+            "us_per_layer": round(us, 4), "gbs": round(gbs, 1), "staged_us_per_layer": round(s_us, 4),
+            "bytes_per_step": nbytes}
 
 
 def attention_leg(torch, mq, wl, args):

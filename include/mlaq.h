@@ -209,8 +209,7 @@ int mlaq_run_ex(const mlaq_run_args* args, void* stream);
  * All 16-byte aligned; out must not overlap an input. Sizes: latent 512,
  * value 128, H in {8, 11, 16}, M in 0..32 (0: no-op). Same status codes,
  * asynchrony, graph-capturability and determinism as mlaq_run.
- * mlaq_uv_prewarm loads the kernels of the listed token counts for both
- * cache hints (see mlaq_uv_run_ex).
+ * mlaq_uv_prewarm loads the kernels of the listed token counts.
  */
 int mlaq_uv_plan_supported(int num_heads, int max_m, int latent_dim, int v_dim, int weight_format,
                            const char* arch);
@@ -220,11 +219,11 @@ int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weig
 int mlaq_uv_run(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
                 int weight_format, void* stream);
 /*
- * mlaq_uv_run with a cache hint (MLAQ_CACHE_*, as for mlaq_run_ex; timing
- * only, results bit-identical; anything else is MLAQ_ERR_INVALID_ARG).
- * MLAQ_CACHE_STREAM, for W_UV read once per decode step and cold in HBM,
- * loads BF16 W_UV rows with the nontemporal hint; MXFP8 weights ignore it.
- * mlaq_uv_run is this call with MLAQ_CACHE_DEFAULT.
+ * mlaq_uv_run with a cache hint (MLAQ_CACHE_*, as for mlaq_run_ex; anything
+ * else is MLAQ_ERR_INVALID_ARG). The hint is accepted so that a caller can
+ * pass one policy to every projection of a layer, and the UV kernels ignore
+ * it: nontemporal W_UV loads measured slower both warm and with every layer
+ * of a decode step cold. mlaq_uv_run is this call with MLAQ_CACHE_DEFAULT.
  */
 int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, void* out, int M, int H,
                    int weight_format, int cache_hint, void* stream);

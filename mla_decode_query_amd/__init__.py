@@ -337,9 +337,9 @@ def mlaq_uv_run(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor |
 def mlaq_uv_run_ex(x: torch.Tensor, w_uv: torch.Tensor, w_uv_scales: torch.Tensor | None, out: torch.Tensor,
                    weight_format: int, stream: torch.cuda.Stream | None = None,
                    cache_hint: int = MLAQ_CACHE_DEFAULT) -> None:
-    """mlaq_uv_run with a cache hint: MLAQ_CACHE_STREAM when W_UV is read once
-    per decode step (cold in HBM), MLAQ_CACHE_DEFAULT otherwise; results are
-    identical."""
+    """mlaq_uv_run with a cache hint (MLAQ_CACHE_DEFAULT or MLAQ_CACHE_STREAM),
+    accepted so that one policy can be passed to every projection of a layer;
+    the UV kernels ignore it (results and timing are those of mlaq_uv_run)."""
     M, H = _uv_views(x, w_uv, w_uv_scales, out, weight_format)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(library().mlaq_uv_run_ex(_ptr(x), _ptr(w_uv), _ptr(w_uv_scales), _ptr(out), M, H, weight_format,

@@ -322,11 +322,9 @@ int mlaq_uv_prewarm(int num_heads, const int* m_regimes, int n_regimes, int weig
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != device) e = hipSetDevice(device);
-    for (bool stream : {false, true}) {
-      const void* fn = mlaq::uv_kernel_for(weight_format, m_regimes[i] <= 16 ? 1 : 2, stream);
-      hipFuncAttributes attr;
-      if (e == hipSuccess && fn) e = hipFuncGetAttributes(&attr, fn);
-    }
+    const void* fn = mlaq::uv_kernel_for(weight_format, m_regimes[i] <= 16 ? 1 : 2);
+    hipFuncAttributes attr;
+    if (e == hipSuccess && fn) e = hipFuncGetAttributes(&attr, fn);
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(MLAQ_ERR_DEVICE, "loading kernel for M=%d: %s", m_regimes[i], hipGetErrorString(e));
   }
@@ -369,8 +367,7 @@ int mlaq_uv_run_ex(const void* x, const void* w_uv, const void* w_uv_scales, voi
   st = mlaq_uv_plan_supported(H, M, MLAQ_LATENT_DIM, MLAQ_V_DIM, weight_format, arch);
   if (st != MLAQ_OK) return st;
   const int m_tiles = M <= 16 ? 1 : 2;
-  const bool nt = cache_hint == MLAQ_CACHE_STREAM && weight_format == MLAQ_WEIGHT_BF16;
-  const void* fn = mlaq::uv_kernel_for(weight_format, m_tiles, nt);
+  const void* fn = mlaq::uv_kernel_for(weight_format, m_tiles); // the cache hint is validated above, not used
   if (!fn) return fail(MLAQ_ERR_UNSUPPORTED, "no kernel for this plan");
   dim3 grid, block;
   mlaq::uv_launch_shape(H, m_tiles, &grid, &block);

@@ -69,10 +69,9 @@ struct UvArgs {
   int H;
 };
 
-// V up-projection kernel for a weight format and M tile count, and its grid.
-// stream: the nontemporal BF16-weight kernel (MLAQ_CACHE_STREAM); MXFP8 has
-// only the ordinary one (nullptr when asked for a streaming MXFP8 kernel).
-const void* uv_kernel_for(int weight_format, int m_tiles, bool stream = false);
+// V up-projection kernel for a weight format and M tile count, and its grid
+// (one kernel per pair: the cache hint does not select a UV kernel).
+const void* uv_kernel_for(int weight_format, int m_tiles);
 void uv_launch_shape(int H, int m_tiles, dim3* grid, dim3* block);
 
 // Dense MLA decode attention (all tensors contiguous in their inner

@@ -59,11 +59,14 @@ constexpr int kUvSpan = 512 / kUvWaves; // latent values per wave
 static_assert(kUvWaves == 1 || kUvWaves == 2 || kUvWaves == 4 || kUvWaves == 8, "k-blocks split evenly");
 constexpr int kUvScalesPerRow = kLatent / kMxBlock;
 
-// NT (MLAQ_CACHE_STREAM, BF16 weights only): the W_UV rows are loaded with
-// the nontemporal hint. Same-box A/B, cold back-to-back layers: 3% shorter
-// BF16 launches (bit-identical), 7.5% longer back-to-back calls on one warm
-// weight set; nontemporal output stores and MXFP8 rows gained nothing.
-template <int WF, int NMT, int CB, bool NT>
+// W_UV rows are loaded with the ordinary cache policy whatever the caller's
+// cache hint. A nontemporal form for BF16 rows was measured: 3% shorter cold
+// BF16 launches only while the other layers' weights stayed in the Infinity
+// Cache (which streamed rows do not claim); with every layer of the step cold
+// it made the BF16 layers ~3% longer (the 64-layer UV step 2.78 -> 2.82 us per
+// layer, three bench runs), and back-to-back calls on one warm weight set
+// 7.5% longer. Nontemporal output stores and MXFP8 rows gained nothing.
+template <int WF, int NMT, int CB>
 __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_t* x, const void* w,
                                                                    const uint8_t* w_scales, void* out, int M_,
                                                                    int H_) {
@@ -74,7 +77,6 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   constexpr int MROWS = 16;        // tokens per workgroup
   constexpr int LDW = CB + 4;
   static_assert(CB == 8 || CB == 16, "8 or 16 value columns per workgroup");
-  static_assert(!NT || WF == MLAQ_WEIGHT_BF16, "only BF16 W_UV rows are streamed nontemporally");
   __shared__ __attribute__((aligned(16))) float part[kUvWaves * MROWS * LDW];
 
   const int tid = threadIdx.x;
@@ -99,12 +101,7 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
   if constexpr (WF == MLAQ_WEIGHT_BF16) {
     const uint32_t off = ((uint32_t(h) * kValue + v) * kLatent + cbase) * 2;
 #pragma unroll
-    for (int kb = 0; kb < kUvKb; ++kb) {
-      if constexpr (NT)
-        wb[kb] = __builtin_nontemporal_load(at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb));
-      else
-        wb[kb] = *at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb);
-    }
+    for (int kb = 0; kb < kUvKb; ++kb) wb[kb] = *at_byte<const u32x4_t>(a.w, off + 2 * kStep * kb);
   } else {
     const uint32_t off = (uint32_t(h) * kValue + v) * kLatent + cbase;
 #pragma unroll
@@ -174,20 +171,17 @@ __global__ __launch_bounds__(kUvThreads) void uv_projection_kernel(const uint16_
 // workgroups at H = 16 either way).
 constexpr int uv_cols(int m_tiles) { return m_tiles == 1 ? 8 : 16; }
 
-template <int WF, int NMT, bool NT = false>
+template <int WF, int NMT>
 const void* uv_kernel_ptr() {
-  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, NMT, uv_cols(NMT), NT>);
+  return reinterpret_cast<const void*>(&uv_projection_kernel<WF, NMT, uv_cols(NMT)>);
 }
 
 } // namespace
 
-const void* uv_kernel_for(int weight_format, int m_tiles, bool stream) {
-  if (weight_format == MLAQ_WEIGHT_BF16) {
-    if (stream)
-      return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1, true>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2, true>();
+const void* uv_kernel_for(int weight_format, int m_tiles) {
+  if (weight_format == MLAQ_WEIGHT_BF16)
     return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_BF16, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_BF16, 2>();
-  }
-  if (weight_format == MLAQ_WEIGHT_MXFP8 && !stream)
+  if (weight_format == MLAQ_WEIGHT_MXFP8)
     return m_tiles == 1 ? uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 1>() : uv_kernel_ptr<MLAQ_WEIGHT_MXFP8, 2>();
   return nullptr;
 }

@@ -147,10 +147,10 @@ def test_uv_can_implement_on_device():
 
 @pytest.mark.parametrize("wf", [WEIGHT_BF16, WEIGHT_MXFP8])
 def test_uv_stream_cache_hint(wf):
-    """mlaq_uv_run_ex with MLAQ_CACHE_STREAM (nontemporal BF16 W_UV loads; the
-    ordinary kernel for MXFP8) gives the oracle's parity and the bits of the
-    default hint for every head count and both token tiles, and leaves the
-    bytes past the output untouched."""
+    """mlaq_uv_run_ex accepts MLAQ_CACHE_STREAM (the UV kernels ignore the
+    hint) and gives the oracle's parity and the bits of the default hint for
+    every head count and both token tiles, leaving the bytes past the output
+    untouched."""
     for H in (8, 11, 16):
         x_all, w, s = uv_inputs(5100 + 10 * H + wf, H, wf)
         wd = dev_bf16(w) if wf == WEIGHT_BF16 else dev_u8(w)
@@ -173,7 +173,7 @@ def test_uv_stream_cache_hint(wf):
 
 
 def test_uv_stream_hint_in_a_graph_with_a_consumer():
-    """Two streaming-hint UV calls captured in one graph, each followed at once
+    """Two UV calls passed the streaming hint, captured in one graph, each followed at once
     by a copy kernel reading its output; replays with new x and W_UV in place
     match the oracle in every copy."""
     H, M, wf = 11, 32, WEIGHT_BF16
