@@ -22,9 +22,10 @@
 // S/4 consecutive c from S w + (S/4) g (c = S w + (S/4) g + 8kb + e), i.e.
 // whole MX scale groups of 32 (four with one wave), in 16-byte loads and one
 // scale byte per group, instead of 8-byte loads and a scale byte for each.
-// (The grouped form made cold BF16 launches with nontemporal loads about 10%
-// longer: each instruction then touches every 128-byte line of a row segment
-// in 16-byte pieces.) The waves' partial tiles are summed through LDS in a
+// (BF16 rows keep the ungrouped form: grouped, with the nontemporal loads
+// they then had, cold BF16 launches ran about 10% longer, each instruction
+// touching every 128-byte line of a row segment in 16-byte pieces; BF16 rows
+// have no scale loads for grouping to save.) The waves' partial tiles are summed through LDS in a
 // fixed order, and the tile goes through LDS anyway so that each thread
 // stores 4 consecutive columns. Every workgroup reads its head's x rows for
 // its tile from L2, which is the per-CU traffic that grows with M, so the
