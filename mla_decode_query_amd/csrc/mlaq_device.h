@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels of libmlaq (mlaq_kernels.hip,
-// mlaq_uv.hip). Not part of the C ABI.
+// mlaq_uv.hip, mlaq_attn.hip). Not part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,7 +14,6 @@ namespace dev {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -123,34 +122,8 @@ __device__ __forceinline__ uint32_t e4m3x2_scaled_bf16(uint32_t word, float scal
 }
 
 // ---------------------------------------------------------------------------
-// Loads
+// Addressing
 // ---------------------------------------------------------------------------
-
-// One lane's segment of one k row: RB bytes (2, 4, 8 or 16) into dwords.
-// NT marks a 4-byte load nontemporal (streamed data, read once).
-template <int RB, bool NT = false>
-__device__ __forceinline__ void load_row(const uint8_t* p, uint32_t (&d)[(RB + 3) / 4]) {
-  static_assert(!NT || RB == 4, "nontemporal row loads are 4 bytes wide");
-  if constexpr (RB == 2) {
-    d[0] = *reinterpret_cast<const uint16_t*>(p);
-  } else if constexpr (RB == 4) {
-    if constexpr (NT)
-      d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-    else
-      d[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (RB == 8) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    d[0] = v[0];
-    d[1] = v[1];
-  } else {
-    static_assert(RB == 16, "row segment must be 2, 4, 8 or 16 bytes");
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    d[0] = v[0];
-    d[1] = v[1];
-    d[2] = v[2];
-    d[3] = v[3];
-  }
-}
 
 // Base pointer + 32-bit byte offset: a uniform base and a zero-extended
 // 32-bit offset let the compiler use the SGPR-base form of global memory ops.
