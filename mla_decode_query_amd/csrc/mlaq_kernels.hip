@@ -153,12 +153,17 @@ __global__ __launch_bounds__(64 * NW) void fused_query_kernel(
   const int pcol = (PB / ESZ) * (lane % LPR); // first tile column of each piece
 
   // 1. This thread's q_pe chunk (8 elements), requested first so that its
-  //    store can leave while the weights are still in flight. Chunk x of the
-  //    head goes to column tile x % NCT, thread x / NCT.
-  const int pe_chunk = ct + NCT * tid;
-  const bool has_pe = pe_chunk < M * (kRope / 8);
-  const int pe_x = has_pe ? pe_chunk : 0;
-  const int pe_m = pe_x >> 3, pe_c = pe_x & 7;
+  //    store can leave while the weights are still in flight. Token m's 8
+  //    chunks go to column tile m % NCT, threads 8 (m / NCT) + c, so one
+  //    workgroup writes each token's whole q_pe piece of the row (one line
+  //    with BF16 output, half a line with E4M3). When a head's tiles straddle
+  //    two XCDs (H = 11), pieces written from two L2s into one line cost
+  //    much more: spreading the chunks over the head's tiles (chunk x to tile
+  //    x % NCT) made H = 11 launches 5-9% longer (same-box A/B, cold: 2.503 vs
+  //    2.365 us at M = 1, 2.944 vs 2.673 us at M = 32), H = 16 equal.
+  const int pe_tok = ct + NCT * (tid >> 3);
+  const bool has_pe = pe_tok < M;
+  const int pe_m = has_pe ? pe_tok : 0, pe_c = tid & 7;
   const uint32_t pe_off = __umul24(pe_m, a.pe_sm) + __umul24(h, a.pe_sh) + 8 * pe_c;
   const u32x4_t pe_v = *at_byte<const u32x4_t>(a.q_pe, 2 * pe_off);
   __builtin_amdgcn_sched_barrier(0);
